@@ -1,0 +1,158 @@
+"""Pins for the oracle's calibration (Eq. 1-5) — CPU only."""
+import numpy as np
+import pytest
+
+from oracle import calibrate as cal
+from oracle import gqa
+from synth import WORKLOADS, make_gqa_calibration, bf16_bits
+from synth.workloads import haar_orthogonal, key_spectrum, query_spectrum, query_amplitude
+
+
+def _rand_spd(d, rng, decay=1.0):
+    u = haar_orthogonal(d, int(rng.integers(1 << 30)))
+    lam = np.arange(1, d + 1, dtype=np.float64) ** -decay * rng.uniform(0.5, 1.5, d)
+    return (u * lam) @ u.T
+
+
+def _haar_projector(d, r, rng):
+    u = haar_orthogonal(d, int(rng.integers(1 << 30)))
+    return u[:, :r] @ u[:, :r].T
+
+
+@pytest.fixture(scope="module")
+def tiny_moments():
+    w = WORKLOADS["tiny"]
+    q, k = make_gqa_calibration(w, 0)
+    q64 = cal.bf16_to_f64(bf16_bits(q))
+    k64 = cal.bf16_to_f64(bf16_bits(k))
+    gq, gk = cal.moments_per_head(q64, k64, w.group)
+    return w, q64, k64, gq, gk
+
+
+def test_bf16_decode_exact():
+    x = np.array([1.0, -2.5, 3.140625, 2.0 ** -100, 0.0, -0.0], dtype=np.float32)
+    u16 = (x.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(cal.bf16_to_f64(u16), x.astype(np.float64))
+
+
+def test_group_mean_contiguous_groups():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((8, 5))
+    m = cal.group_mean(q, 4)
+    # heads 0..3 -> KV head 0, 4..7 -> KV head 1; G=1 is the identity
+    assert np.allclose(m[0], sum(q[i] for i in range(4)) / 4, atol=1e-15)
+    assert np.allclose(m[1], sum(q[i] for i in range(4, 8)) / 4, atol=1e-15)
+    assert np.array_equal(cal.group_mean(q, 1), q)
+
+
+def test_second_moments_match_population(tiny_moments):
+    """Sample second moments vs the generator's closed-form population moments."""
+    w, _, _, gq, gk = tiny_moments
+    d, G = w.head_dim, w.group
+    for h in range(w.num_kv_heads):
+        from synth.workloads import _haar_cached, P_BASIS
+        u = _haar_cached(w.model, 0, h, d, P_BASIS)
+        pop_k = (u * key_spectrum(d) ** 2) @ u.T
+        cq = query_amplitude(d, d)
+        pop_q = (u * (cq ** 2 / G) * query_spectrum(d) ** 2) @ u.T
+        T = w.calib_seqs * w.calib_len
+        for g_hat, pop in ((gk[h], pop_k), (gq[h], pop_q)):
+            rel = np.linalg.norm(g_hat - pop) / np.linalg.norm(pop)
+            # Gaussian sample second moment: E|S - Sigma|_F^2 = (tr(Sigma)^2 + |Sigma|_F^2) / T
+            expect = np.sqrt((np.trace(pop) ** 2 + np.linalg.norm(pop) ** 2) / T) / np.linalg.norm(pop)
+            assert 0.5 * expect < rel < 1.5 * expect, (rel, expect)
+
+
+def test_streamed_moments_equal_batch(tiny_moments):
+    w, q, k, gq, gk = tiny_moments
+    chunks = [(q[i:i + 300], k[i:i + 300]) for i in range(0, q.shape[0], 300)]
+    sq, sk = cal.moments_streamed(chunks, w.group)
+    assert np.allclose(sq, gq, rtol=1e-12, atol=1e-14)
+    assert np.allclose(sk, gk, rtol=1e-12, atol=1e-14)
+
+
+def test_basis_orthonormal_and_sign_rule(tiny_moments):
+    w, _, _, gq, gk = tiny_moments
+    for h in range(w.num_kv_heads):
+        m = cal.basis(gq[h], gk[h], w.rank)
+        assert m.shape == (w.rank, w.head_dim)
+        assert np.abs(m @ m.T - np.eye(w.rank)).max() < 1e-12
+        m32 = m.astype(np.float32).astype(np.float64)
+        assert np.abs(m32 @ m32.T - np.eye(w.rank)).max() < 1e-6
+        for row in m:
+            assert row[np.argmax(np.abs(row))] > 0
+        assert abs(np.trace(cal.unit_trace(gq[h])) - 1) < 1e-12
+
+
+def test_ky_fan_closed_form_and_optimality(tiny_moments):
+    """Eq. 5: L_marg(M*) equals the sum of the trailing eigenvalues and beats any other rank-r projector."""
+    w, _, _, gq, gk = tiny_moments
+    rng = np.random.default_rng(3)
+    d, r = w.head_dim, w.rank
+    for h in range(w.num_kv_heads):
+        a = cal.joint_matrix(gq[h], gk[h])
+        lam = np.sort(np.linalg.eigvalsh(a))[::-1]
+        m = cal.basis(gq[h], gk[h], r)
+        best = cal.l_marg(cal.projector(m), gq[h], gk[h])
+        assert abs(best - lam[r:].sum()) < 1e-12
+        assert abs(lam.sum() - 2.0) < 1e-12          # two unit-trace matrices
+        for _ in range(200):
+            assert cal.l_marg(_haar_projector(d, r, rng), gq[h], gk[h]) >= best - 1e-12
+        from synth.workloads import _haar_cached, P_BASIS
+        u = _haar_cached(w.model, 0, h, d, P_BASIS)
+        pu = u[:, :r] @ u[:, :r].T
+        assert cal.l_marg(pu, gq[h], gk[h]) >= best - 1e-12
+        # the calibrated subspace is close to the generator's leading directions
+        captured = np.linalg.norm(m @ u[:, :r]) ** 2 / r
+        assert captured > 0.8, captured
+
+
+def test_eq4_bound_on_many_projectors(tiny_moments):
+    w, _, _, gq, gk = tiny_moments
+    rng = np.random.default_rng(4)
+    d, r = w.head_dim, w.rank
+    projs = [cal.projector(cal.basis(gq[0], gk[0], r))] + [_haar_projector(d, r, rng) for _ in range(100)]
+    for p in projs:
+        assert cal.l_sel(p, gq[0], gk[0]) <= 0.25 * cal.l_marg(p, gq[0], gk[0]) ** 2 + 1e-14
+    for _ in range(50):                                     # random SPD pairs, random ranks
+        dd = int(rng.integers(4, 24))
+        rr = int(rng.integers(1, dd))
+        a, b = _rand_spd(dd, rng), _rand_spd(dd, rng, 0.5)
+        p = _haar_projector(dd, rr, rng)
+        assert cal.l_sel(p, a, b) >= -1e-14
+        assert cal.l_sel(p, a, b) <= 0.25 * cal.l_marg(p, a, b) ** 2 + 1e-14
+
+
+def test_eq4_equality_case():
+    """A = B = u u^T with u orthogonal to range(P): L_sel = 1 = (1/4) * 2^2."""
+    d, r = 10, 3
+    u = haar_orthogonal(d, 11)
+    p = u[:, :r] @ u[:, :r].T
+    v = u[:, r + 2]
+    a = np.outer(v, v)
+    assert abs(cal.l_sel(p, a, a) - 1.0) < 1e-12
+    assert abs(cal.l_marg(p, a, a) - 2.0) < 1e-12
+
+
+def test_eq2_score_error_identity(tiny_moments):
+    """s - s^ = qbar^T (I - P) k with s^ = (M qbar).(M k) from the oracle's projected query."""
+    w, _, _, gq, gk = tiny_moments
+    rng = np.random.default_rng(5)
+    m = np.stack([cal.basis(gq[h], gk[h], w.rank) for h in range(w.num_kv_heads)]).astype(np.float32)
+    q = rng.standard_normal((w.num_q_heads, w.head_dim)).astype(np.float32)
+    q_u16 = (q.view(np.uint32) >> 16).astype(np.uint16)
+    qhat = gqa.project_query(q_u16, m, w.group)
+    q64 = cal.bf16_to_f64(q_u16)
+    for h in range(w.num_kv_heads):
+        qbar = q64[h * w.group:(h + 1) * w.group].mean(0)
+        mh = m[h].astype(np.float64)
+        p = mh.T @ mh
+        for _ in range(20):
+            k = rng.standard_normal(w.head_dim)
+            s_hat = qhat[h] @ (mh @ k)
+            s = qbar @ k
+            assert abs((s - s_hat) - qbar @ (np.eye(w.head_dim) - p) @ k) < 1e-12
+    # r = d with M = I reproduces the exact score qbar . k
+    eye = np.stack([np.eye(w.head_dim, dtype=np.float32)] * w.num_kv_heads)
+    qh = gqa.project_query(q_u16, eye, w.group)
+    assert np.allclose(qh[1], q64[w.group:2 * w.group].mean(0), atol=1e-15)
