@@ -1,0 +1,203 @@
+/*
+ * jssa.h — C ABI of the Joint Subspace Sparse Attention (JSSA) decode hot path
+ * on AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * Method (paper summary page "Summary (Overview)" of arXiv 2610.19026,
+ * §3.1 Overview): for every layer and KV head keep an FP8 cache of keys
+ * projected onto an r-dim orthonormal basis M (K_proj = K M^T, §3.4); at each
+ * decode step average the G query heads of the KV head, project the mean with
+ * M, score every cached token against K_proj (Eq. 1), keep the top-B
+ * positions of that KV head, and attend the full-dimensional queries of the
+ * group to those positions in place in the paged bf16 KV cache (§3.3,
+ * "gather-free indexed attention").  M comes from calibration (Eq. 5).
+ *
+ * Conventions for every entry point
+ *   - Tensor arguments are DEVICE pointers owned by the caller unless a
+ *     function says "host".  Row-major, densely packed.  bf16 is passed as
+ *     uint16_t bit patterns.  FP8 is OCP E4M3FN.
+ *   - Work is enqueued asynchronously on `stream`; no function synchronises,
+ *     allocates device memory or keeps state between calls (the library caches
+ *     nothing but device properties).  Calls are thread-safe; two calls that
+ *     share a workspace must be ordered by the caller.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     error nothing is enqueued and a negative jssa_status is returned.
+ *     A failed launch returns JSSA_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Caller obligations that are NOT checked on the device: every
+ *     block_table entry used (positions < seq_lens[b]) names a valid page;
+ *     seq_lens[b] <= max_pages_per_seq * page_size (larger values are clamped);
+ *     indices hold positions < seq_lens[b] or -1.
+ *   - Positions are logical token positions within a sequence; a position t
+ *     lives in page block_table[b][t / page_size], slot t % page_size.
+ *
+ * Shapes (GQA): q [batch, Hq, d]; k_cache, v_cache [num_pages, page, Hkv, d]
+ * (one token's slice is contiguous over d, the standard paged GQA layout);
+ * block_table int32 [batch, max_pages_per_seq]; seq_lens int32 [batch]
+ * (N, including the token being decoded); M fp32 [Hkv, r, d].
+ * Shapes (MLA, kind = JSSA_KIND_MLA): Hkv = 1, d = 576 = 512 latent + 64 RoPE;
+ * q [batch, Hq, 576]; k_cache = latent cache [num_pages, page, 576];
+ * M fp32 [r, 512] acting on the latent part; outputs have 512 dims.
+ *
+ * Projected scoring cache (written by jssa_store, read by jssa_select):
+ *   kp       uint8 [num_pages, Hkv, S/16, page, 16]   (S = scoring dims:
+ *            r for GQA, r + 64 for MLA; 16-byte pieces, piece-major inside
+ *            one (page, KV head) block so a wavefront reads it contiguously)
+ *   kp_scale fp32  [num_pages, Hkv, page]
+ *   The element i of the projected key of (page p, slot s, head h) is
+ *   kp[p][h][i/16][s][i%16] * kp_scale[p][h][s].
+ */
+#ifndef JSSA_H_
+#define JSSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JSSA_OK = 0,
+  JSSA_ERR_NULL = -1,         /* a required pointer is NULL */
+  JSSA_ERR_SHAPE = -2,        /* inconsistent sizes (e.g. Hq % Hkv != 0, budget <= 0) */
+  JSSA_ERR_UNSUPPORTED = -3,  /* valid but not built (e.g. d not in {128, 256}) */
+  JSSA_ERR_WORKSPACE = -4,    /* workspace smaller than jssa_workspace_bytes() */
+  JSSA_ERR_HIP = -5           /* a HIP launch or runtime call failed */
+} jssa_status;
+
+enum { JSSA_KIND_GQA = 0, JSSA_KIND_MLA = 1 };
+
+/* jssa_select strategies (both return the same set):
+ *   AUTO          sampled threshold + candidate compaction in one pass over the
+ *                 FP8 cache, exact top-B of the candidates in LDS; falls back to
+ *                 EXACT_STREAM per (sequence, KV head) whenever the candidate
+ *                 set could miss a member of the top-B.
+ *   EXACT_STREAM  per (sequence, KV head) radix select over recomputed scores
+ *                 (several passes over the FP8 cache; slow, data independent). */
+enum { JSSA_SELECT_AUTO = 0, JSSA_SELECT_EXACT_STREAM = 1 };
+
+typedef struct jssa_shape {
+  int32_t kind;               /* JSSA_KIND_GQA or JSSA_KIND_MLA */
+  int32_t batch;              /* sequences in the step, >= 1 */
+  int32_t num_q_heads;        /* Hq; GQA: Hq % Hkv == 0, G = Hq/Hkv in {1,2,4,8}; MLA: multiple of 16, <= 128 */
+  int32_t num_kv_heads;       /* Hkv; MLA: 1 */
+  int32_t head_dim;           /* d: GQA 128 or 256; MLA 576 */
+  int32_t page_size;          /* tokens per page: 16, 32 or 64 */
+  int32_t max_pages_per_seq;  /* row stride of block_table */
+  int32_t rank;               /* r: GQA r % 16 == 0, r <= min(d, 128); MLA latent rank, 64 */
+  int32_t budget;             /* B: 1..4096 */
+  int32_t select_mode;        /* JSSA_SELECT_AUTO or JSSA_SELECT_EXACT_STREAM */
+} jssa_shape;
+
+/* Human-readable name of a jssa_status value (static string, never NULL). */
+const char* jssa_status_string(int32_t status);
+
+/* Bytes of device workspace that jssa_select / jssa_attend / jssa_decode /
+ * jssa_full_decode need for this shape (all positions < max_pages_per_seq *
+ * page_size).  Writes *bytes; returns a jssa_status. */
+int32_t jssa_workspace_bytes(const jssa_shape* shape, size_t* bytes);
+
+/* Bytes of the projected scoring cache per page (kp) and fp32 scales per page
+ * (kp_scale elements), so callers can size both buffers. */
+int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page,
+                           int64_t* scale_elems_per_page);
+
+/* jssa_store — project new keys with M and append them, FP8-quantised, to the
+ * scoring cache (summary page §3.4: K_proj = K M^T, kept in FP8).
+ *   GQA: y = M_h k (fp32 accumulate); MLA: y = [M c ; k_pe] (128 dims).
+ *   scale = max_i |y_i| / 448 (fp32), codes = E4M3FN(y / scale), round to
+ *   nearest even, saturating; an all-zero y stores scale 0 and zero codes.
+ * k_new : GQA bf16 [T, Hkv, d]; MLA bf16 [T, 576]
+ * slot  : int32 [T], physical page * page_size + slot in page; < 0 skips the row
+ * M     : GQA fp32 [Hkv, r, d]; MLA fp32 [r, 512]
+ * kp, kp_scale : the scoring cache (layout above), written at the slots only. */
+int32_t jssa_store(const jssa_shape* shape, const uint16_t* k_new, const int32_t* slot, int32_t T,
+                   const float* M, uint8_t* kp, float* kp_scale, hipStream_t stream);
+
+/* jssa_select — per (sequence b, KV head h): qbar = mean of the G query heads
+ * of h (heads h*G .. h*G+G-1), qhat = M_h qbar (fp32; MLA: [M qbar[:512];
+ * qbar[512:]]), score s_t = kp_scale_t * sum_i qhat_i * kp_t,i (fp32) for
+ * every position t < seq_lens[b], then the min(B, N) positions with the
+ * largest score (summary page §3.1 steps 1-2, Eq. 1).  Ties at the B-th
+ * score go to the lowest position; -0 counts as +0.
+ * indices   : out int32 [batch, Hkv, B], ascending positions, -1 padded
+ * scores_out: optional out fp32 [batch, Hkv, max_pages_per_seq*page] (NULL: not
+ *             written); positions >= seq_lens[b] are left untouched. */
+int32_t jssa_select(const jssa_shape* shape, const uint16_t* q, const float* M, const uint8_t* kp,
+                    const float* kp_scale, const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t* indices, float* scores_out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* jssa_select_stages — the three phases of jssa_select, for callers that time
+ * or interleave them: JSSA_STAGE_PROLOGUE (qhat and the sampled threshold),
+ * JSSA_STAGE_STREAM (FP8 score stream over every cached token + candidate
+ * compaction), JSSA_STAGE_FINISH (exact top-B from the candidates, or the
+ * exact re-scoring fallback).  `stages` is a bit mask; phases run in that
+ * order, and a phase reads what the previous phase left in `workspace`, so
+ * one jssa_select equals PROLOGUE, STREAM, FINISH issued in order on one
+ * stream with the same arguments.  Other arguments as jssa_select. */
+enum { JSSA_STAGE_PROLOGUE = 1, JSSA_STAGE_STREAM = 2, JSSA_STAGE_FINISH = 4, JSSA_STAGE_ALL = 7 };
+int32_t jssa_select_stages(const jssa_shape* shape, int32_t stages, const uint16_t* q, const float* M,
+                           const uint8_t* kp, const float* kp_scale, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t* indices, float* scores_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* jssa_attend — gather-free indexed attention (summary page §3.3): query head
+ * j attends, with exact softmax, over the positions that its KV head h = j/G
+ * selected, reading K/V rows in place through the block table.  Logits are
+ * sm_scale * q_j . k_t; out = sum softmax * v_t.  GQA out bf16 [batch, Hq, d];
+ * MLA keys are the 576-dim latent rows, values their first 512 dims, out bf16
+ * [batch, Hq, 512] (v_cache ignored, may be NULL).  lse_out (optional, fp32
+ * [batch, Hq], natural log) receives log sum exp of the logits.  An empty set
+ * gives out = 0 and lse = -inf.
+ * indices : int32 [batch, Hkv, B] as written by jssa_select (-1 entries skipped). */
+int32_t jssa_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
+                    const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* indices, float sm_scale, uint16_t* out, float* lse_out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* jssa_decode — one decode step: [jssa_store of k_new at slot_new, skipped when
+ * k_new is NULL] -> jssa_select -> jssa_attend, all on `stream`.  k_new holds
+ * one new key per sequence (T = batch), i.e. the token at position
+ * seq_lens[b]-1, so the token being decoded is itself eligible for selection. */
+int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_new,
+                    const int32_t* slot_new, const float* M, uint8_t* kp, float* kp_scale,
+                    const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* block_table,
+                    const int32_t* seq_lens, int32_t* indices, float sm_scale, uint16_t* out,
+                    float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* jssa_full_decode — the dense baseline (README page §3, "Full-KV" decode):
+ * the same attention over every position t < N (window == 0) or over the
+ * last `window` positions [N - window, N) (window > 0: sliding-window layers,
+ * which keep dense attention).  GQA only. */
+int32_t jssa_full_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                         int32_t window, float sm_scale, uint16_t* out, float* lse_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* jssa_calib_moments — calibration second moments (summary page §3.2; README
+ * page §2): ADDS sum_t qbar_t qbar_t^T to gq and sum_t k_t k_t^T to gk (fp32,
+ * [Hkv, dm, dm]; dm = d, MLA dm = 512 over the latent dims), so a long
+ * calibration set can be streamed in chunks; the caller zero-initialises gq, gk.
+ * The 1/T of the second moment is left out: the basis normalises each moment
+ * to unit trace, which cancels it.
+ * q_cal : bf16 [T, Hq, d] (MLA [T, Hq, 576]); k_cal : bf16 [T, Hkv, d] (MLA [T, 576]).
+ * workspace: at least jssa_calib_workspace_bytes(shape, T) bytes (fp32 staging). */
+int32_t jssa_calib_workspace_bytes(const jssa_shape* shape, int32_t T, size_t* bytes);
+int32_t jssa_calib_moments(const jssa_shape* shape, const uint16_t* q_cal, const uint16_t* k_cal,
+                           int32_t T, float* gq, float* gk, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* jssa_basis — HOST function: M* = TopEig_r(G~_Qbar + G~_K)^T (summary page
+ * Eq. 5), each moment normalised to unit trace, per KV head, eigenvectors as
+ * rows in descending eigenvalue order, each row's largest-magnitude entry made
+ * positive.  gq, gk: HOST fp32 [Hkv, dm, dm] (dm = d, MLA 512), as summed by
+ * jssa_calib_moments; M_out: HOST fp32 [Hkv, r, dm].  Symmetric eigensolver in
+ * double precision (Householder tridiagonalisation + implicit QL). */
+int32_t jssa_basis(const jssa_shape* shape, const float* gq, const float* gk, float* M_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JSSA_H_ */

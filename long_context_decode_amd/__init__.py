@@ -1,0 +1,12 @@
+"""JSSA decode hot path on MI355X (gfx950): Python binding of libjssa.so.
+
+The names mirror the C ABI in include/jssa.h; the library's HIP kernels do all
+of the work.  Importing this package fails if libjssa.so has not been built.
+"""
+from ._lib import (  # noqa: F401
+    KIND_GQA, KIND_MLA, SELECT_AUTO, SELECT_EXACT_STREAM, STAGE_PROLOGUE, STAGE_STREAM, STAGE_FINISH, STAGE_ALL,
+    MLA_LATENT, MLA_ROPE, EXPORTED, LIB_PATH,
+    JSSAError, Shape, make_shape, shape_for, status_string, workspace_bytes, kp_page_bytes, alloc_workspace,
+    alloc_scoring_cache, jssa_store, jssa_select, jssa_attend, jssa_decode, jssa_full_decode,
+    calib_workspace_bytes, jssa_calib_moments, jssa_basis, raw_library,
+)

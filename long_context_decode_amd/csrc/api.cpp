@@ -1,0 +1,378 @@
+// C ABI of the JSSA decode path: host-side validation, launch planning and
+// workspace layout.  Every check runs before anything is enqueued; kernels are
+// launched asynchronously on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/jssa.h"
+#include "kernels.h"
+
+namespace jssa {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int kind, batch, Hq, Hkv, d, P, max_pages, r, S, B, G, mla, dv;
+  int64_t maxN;
+  int cp, max_chunks;
+  int sp_splits, sp_len;     // sparse attention split plan
+  int dn_splits, dn_len;     // dense (window 0) split plan
+  size_t off_qhat, off_tau, off_counter, off_chunk, off_ckey, off_cidx, off_part_o, off_part_ml, total;
+};
+
+void split_plan(int64_t n_tok_max, int pairs, int* splits, int* len) {
+  if (n_tok_max <= 0) {
+    *splits = 1;
+    *len = 64;
+    return;
+  }
+  int64_t s = cdiv(2048, std::max(pairs, 1));
+  s = std::min<int64_t>(s, cdiv(n_tok_max, 64));
+  s = std::max<int64_t>(1, std::min<int64_t>(s, 256));
+  int64_t l = cdiv(cdiv(n_tok_max, s), 64) * 64;
+  *len = (int)l;
+  *splits = (int)cdiv(n_tok_max, l);
+}
+
+int32_t validate_shape(const jssa_shape* sh) {
+  if (!sh) return JSSA_ERR_NULL;
+  if (sh->kind != JSSA_KIND_GQA && sh->kind != JSSA_KIND_MLA) return JSSA_ERR_UNSUPPORTED;
+  if (sh->batch < 1 || sh->num_q_heads < 1 || sh->num_kv_heads < 1 || sh->max_pages_per_seq < 1)
+    return JSSA_ERR_SHAPE;
+  if (sh->num_q_heads % sh->num_kv_heads != 0) return JSSA_ERR_SHAPE;
+  if (sh->budget < 1 || sh->budget > 4096) return JSSA_ERR_SHAPE;
+  if (sh->page_size != 16 && sh->page_size != 32 && sh->page_size != 64) return JSSA_ERR_UNSUPPORTED;
+  if (sh->select_mode != JSSA_SELECT_AUTO && sh->select_mode != JSSA_SELECT_EXACT_STREAM) return JSSA_ERR_SHAPE;
+  if (sh->rank < 16 || sh->rank % 16 != 0) return JSSA_ERR_UNSUPPORTED;
+  if (sh->kind == JSSA_KIND_GQA) {
+    if (sh->head_dim != 128 && sh->head_dim != 256) return JSSA_ERR_UNSUPPORTED;
+    const int g = sh->num_q_heads / sh->num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return JSSA_ERR_UNSUPPORTED;
+    if (sh->rank > std::min(sh->head_dim, 128)) return JSSA_ERR_UNSUPPORTED;
+  } else {
+    if (sh->num_kv_heads != 1 || sh->head_dim != kMlaLatent + kMlaRope) return JSSA_ERR_UNSUPPORTED;
+    if (sh->num_q_heads % 16 != 0 || sh->num_q_heads > 128) return JSSA_ERR_UNSUPPORTED;
+    if (sh->rank > 64) return JSSA_ERR_UNSUPPORTED;
+  }
+  return JSSA_OK;
+}
+
+int32_t make_plan(const jssa_shape* sh, Plan* p) {
+  const int32_t st = validate_shape(sh);
+  if (st != JSSA_OK) return st;
+  p->kind = sh->kind;
+  p->mla = sh->kind == JSSA_KIND_MLA;
+  p->batch = sh->batch;
+  p->Hq = sh->num_q_heads;
+  p->Hkv = sh->num_kv_heads;
+  p->d = sh->head_dim;
+  p->P = sh->page_size;
+  p->max_pages = sh->max_pages_per_seq;
+  p->r = sh->rank;
+  p->S = p->mla ? sh->rank + kMlaRope : sh->rank;
+  p->B = sh->budget;
+  p->G = p->Hq / p->Hkv;
+  p->dv = p->mla ? kMlaLatent : p->d;
+  p->maxN = (int64_t)p->max_pages * p->P;
+  // stream chunking: aim for >= 2048 blocks, chunk of 4..64 pages
+  const int hpw = 64 / p->P;
+  const int hg = (p->Hkv + hpw - 1) / hpw;
+  int cp = 64;
+  while (cp > 4 && (int64_t)p->batch * hg * cdiv(p->max_pages, cp) < 2048) cp /= 2;
+  while (cdiv(p->max_pages, cp) > kMaxChunks && cp < 64) cp *= 2;
+  if (cdiv(p->max_pages, cp) > kMaxChunks) return JSSA_ERR_UNSUPPORTED;
+  p->cp = cp;
+  p->max_chunks = (int)cdiv(p->max_pages, cp);
+  split_plan(std::min<int64_t>(p->B, p->maxN), p->batch * p->Hkv, &p->sp_splits, &p->sp_len);
+  split_plan(p->maxN, p->batch * p->Hkv, &p->dn_splits, &p->dn_len);
+  const int max_splits = std::max(p->sp_splits, p->dn_splits);
+  const size_t bh = (size_t)p->batch * p->Hkv;
+  size_t off = 0;
+  p->off_qhat = off;    off = align_up(off + bh * p->S * sizeof(float));
+  p->off_tau = off;     off = align_up(off + bh * sizeof(uint32_t));
+  p->off_counter = off; off = align_up(off + bh * sizeof(uint32_t));
+  p->off_chunk = off;   off = align_up(off + bh * p->max_chunks * 2 * sizeof(int32_t));
+  p->off_ckey = off;    off = align_up(off + bh * kCandCap * sizeof(uint32_t));
+  p->off_cidx = off;    off = align_up(off + bh * kCandCap * sizeof(int32_t));
+  const size_t pj = (size_t)p->batch * p->Hq * max_splits;
+  p->off_part_o = off;  off = align_up(off + pj * p->dv * sizeof(float));
+  p->off_part_ml = off; off = align_up(off + pj * 2 * sizeof(float));
+  p->total = off;
+  return JSSA_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? JSSA_OK : JSSA_ERR_HIP; }
+
+int32_t do_store(const Plan& p, const uint16_t* k_new, const int32_t* slot, int32_t T, const float* M,
+                 uint8_t* kp, float* kp_scale, hipStream_t stream) {
+  if (T < 0) return JSSA_ERR_SHAPE;
+  if (T == 0) return JSSA_OK;
+  if (!k_new || !slot || !M || !kp || !kp_scale) return JSSA_ERR_NULL;
+  StoreArgs a{};
+  a.k_new = k_new;
+  a.slot = slot;
+  a.M = M;
+  a.kp = kp;
+  a.kp_scale = kp_scale;
+  a.T = T;
+  a.Hkv = p.Hkv;
+  a.P = p.P;
+  a.d = p.d;
+  a.r = p.r;
+  a.S = p.S;
+  a.mla = p.mla;
+  return hip_status(launch_store(a, stream));
+}
+
+int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q, const float* M, const uint8_t* kp,
+                  const float* kp_scale, const int32_t* block_table, const int32_t* seq_lens, int32_t* indices,
+                  float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !M || !kp || !kp_scale || !block_table || !seq_lens || !indices || !ws) return JSSA_ERR_NULL;
+  if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
+  SelectArgs a{};
+  a.q = q;
+  a.M = M;
+  a.kp = kp;
+  a.kp_scale = kp_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.indices = indices;
+  a.scores_out = scores_out;
+  a.qhat = at<float>(ws, p.off_qhat);
+  a.tau = at<uint32_t>(ws, p.off_tau);
+  a.counter = at<uint32_t>(ws, p.off_counter);
+  a.chunk_tab = at<int32_t>(ws, p.off_chunk);
+  a.cand_key = at<uint32_t>(ws, p.off_ckey);
+  a.cand_idx = at<int32_t>(ws, p.off_cidx);
+  a.batch = p.batch;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.d = p.d;
+  a.P = p.P;
+  a.max_pages = p.max_pages;
+  a.r = p.r;
+  a.S = p.S;
+  a.B = p.B;
+  a.G = p.G;
+  a.mla = p.mla;
+  a.cp = p.cp;
+  a.max_chunks = p.max_chunks;
+  a.force_exact = select_mode == JSSA_SELECT_EXACT_STREAM;
+  return hip_status(launch_select(a, stages, stream));
+}
+
+int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, int window,
+                  float sm_scale, uint16_t* out, float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (p.mla) return JSSA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !ws) return JSSA_ERR_NULL;
+  if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
+  if (window < 0) return JSSA_ERR_SHAPE;
+  AttendArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.indices = indices;
+  a.part_o = at<float>(ws, p.off_part_o);
+  a.part_ml = at<float>(ws, p.off_part_ml);
+  a.out = out;
+  a.lse_out = lse_out;
+  a.sm_log2 = sm_scale * 1.44269504088896340736f;
+  a.batch = p.batch;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.P = p.P;
+  a.max_pages = p.max_pages;
+  a.B = p.B;
+  a.G = p.G;
+  a.window = indices ? 0 : window;
+  if (indices) {
+    a.splits = p.sp_splits;
+    a.split_len = p.sp_len;
+  } else if (window > 0) {
+    split_plan(std::min<int64_t>(window, p.maxN), p.batch * p.Hkv, &a.splits, &a.split_len);
+  } else {
+    a.splits = p.dn_splits;
+    a.split_len = p.dn_len;
+  }
+  return hip_status(launch_attend(a, p.d, stream));
+}
+
+}  // namespace
+}  // namespace jssa
+
+using namespace jssa;
+
+extern "C" {
+
+const char* jssa_status_string(int32_t status) {
+  switch (status) {
+    case JSSA_OK: return "ok";
+    case JSSA_ERR_NULL: return "null pointer argument";
+    case JSSA_ERR_SHAPE: return "inconsistent shape";
+    case JSSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case JSSA_ERR_WORKSPACE: return "workspace too small";
+    case JSSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t jssa_workspace_bytes(const jssa_shape* shape, size_t* bytes) {
+  if (!bytes) return JSSA_ERR_NULL;
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  *bytes = p.total;
+  return JSSA_OK;
+}
+
+int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page, int64_t* scale_elems_per_page) {
+  if (!kp_bytes_per_page || !scale_elems_per_page) return JSSA_ERR_NULL;
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  *kp_bytes_per_page = (int64_t)p.Hkv * p.P * p.S;
+  *scale_elems_per_page = (int64_t)p.Hkv * p.P;
+  return JSSA_OK;
+}
+
+int32_t jssa_store(const jssa_shape* shape, const uint16_t* k_new, const int32_t* slot, int32_t T, const float* M,
+                   uint8_t* kp, float* kp_scale, hipStream_t stream) {
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  return do_store(p, k_new, slot, T, M, kp, kp_scale, stream);
+}
+
+int32_t jssa_select(const jssa_shape* shape, const uint16_t* q, const float* M, const uint8_t* kp,
+                    const float* kp_scale, const int32_t* block_table, const int32_t* seq_lens, int32_t* indices,
+                    float* scores_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  return do_select(p, shape->select_mode, JSSA_STAGE_ALL, q, M, kp, kp_scale, block_table, seq_lens, indices,
+                   scores_out, workspace, workspace_bytes, stream);
+}
+
+int32_t jssa_select_stages(const jssa_shape* shape, int32_t stages, const uint16_t* q, const float* M,
+                           const uint8_t* kp, const float* kp_scale, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t* indices, float* scores_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  if (stages < 0 || stages > JSSA_STAGE_ALL) return JSSA_ERR_SHAPE;
+  return do_select(p, shape->select_mode, stages, q, M, kp, kp_scale, block_table, seq_lens, indices, scores_out,
+                   workspace, workspace_bytes, stream);
+}
+
+int32_t jssa_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                    const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, float sm_scale,
+                    uint16_t* out, float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  if (!indices) return JSSA_ERR_NULL;
+  return do_attend(p, q, k_cache, v_cache, block_table, seq_lens, indices, 0, sm_scale, out, lse_out, workspace,
+                   workspace_bytes, stream);
+}
+
+int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_new, const int32_t* slot_new,
+                    const float* M, uint8_t* kp, float* kp_scale, const uint16_t* k_cache, const uint16_t* v_cache,
+                    const int32_t* block_table, const int32_t* seq_lens, int32_t* indices, float sm_scale,
+                    uint16_t* out, float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  // validate everything before the first launch
+  if (!q || !M || !kp || !kp_scale || !k_cache || !block_table || !seq_lens || !indices || !out || !workspace)
+    return JSSA_ERR_NULL;
+  if (!p.mla && !v_cache) return JSSA_ERR_NULL;
+  if (k_new && !slot_new) return JSSA_ERR_NULL;
+  if (workspace_bytes < p.total) return JSSA_ERR_WORKSPACE;
+  if (p.mla) return JSSA_ERR_UNSUPPORTED;
+  if (k_new) {
+    st = do_store(p, k_new, slot_new, p.batch, M, kp, kp_scale, stream);
+    if (st != JSSA_OK) return st;
+  }
+  st = do_select(p, shape->select_mode, JSSA_STAGE_ALL, q, M, kp, kp_scale, block_table, seq_lens, indices, nullptr, workspace,
+                 workspace_bytes, stream);
+  if (st != JSSA_OK) return st;
+  return do_attend(p, q, k_cache, v_cache, block_table, seq_lens, indices, 0, sm_scale, out, lse_out, workspace,
+                   workspace_bytes, stream);
+}
+
+int32_t jssa_full_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens, int32_t window,
+                         float sm_scale, uint16_t* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  if (p.mla) return JSSA_ERR_UNSUPPORTED;
+  return do_attend(p, q, k_cache, v_cache, block_table, seq_lens, nullptr, window, sm_scale, out, lse_out, workspace,
+                   workspace_bytes, stream);
+}
+
+int32_t jssa_calib_workspace_bytes(const jssa_shape* shape, int32_t T, size_t* bytes) {
+  if (!bytes) return JSSA_ERR_NULL;
+  const int32_t st = validate_shape(shape);
+  if (st != JSSA_OK) return st;
+  if (T < 0) return JSSA_ERR_SHAPE;
+  const int dm = shape->kind == JSSA_KIND_MLA ? kMlaLatent : shape->head_dim;
+  *bytes = align_up((size_t)T * shape->num_kv_heads * dm * sizeof(float)) * 2;
+  return JSSA_OK;
+}
+
+int32_t jssa_calib_moments(const jssa_shape* shape, const uint16_t* q_cal, const uint16_t* k_cal, int32_t T,
+                           float* gq, float* gk, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  const int32_t st = jssa_calib_workspace_bytes(shape, T, &need);
+  if (st != JSSA_OK) return st;
+  if (T == 0) return JSSA_OK;
+  if (!q_cal || !k_cal || !gq || !gk || !workspace) return JSSA_ERR_NULL;
+  if (workspace_bytes < need) return JSSA_ERR_WORKSPACE;
+  CalibArgs a{};
+  a.q = q_cal;
+  a.k = k_cal;
+  a.gq = gq;
+  a.gk = gk;
+  a.T = T;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.d = shape->head_dim;
+  a.mla = shape->kind == JSSA_KIND_MLA;
+  a.dm = a.mla ? kMlaLatent : a.d;
+  a.G = a.Hq / a.Hkv;
+  a.xq = static_cast<float*>(workspace);
+  a.xk = at<float>(workspace, need / 2);
+  return hip_status(launch_calib(a, stream));
+}
+
+int32_t jssa_basis(const jssa_shape* shape, const float* gq, const float* gk, float* M_out) {
+  const int32_t st = validate_shape(shape);
+  if (st != JSSA_OK) return st;
+  if (!gq || !gk || !M_out) return JSSA_ERR_NULL;
+  const int dm = shape->kind == JSSA_KIND_MLA ? kMlaLatent : shape->head_dim;
+  if (shape->rank > dm) return JSSA_ERR_SHAPE;
+  try {
+    return basis_impl(shape->num_kv_heads, dm, shape->rank, gq, gk, M_out);
+  } catch (...) {                        // allocation failure inside the solver
+    return JSSA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// Device helpers shared by the JSSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jssa {
+
+constexpr int kWave = 64;
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- FP8 (OCP E4M3FN on gfx950)
+
+// Four codes packed little-endian in a dword -> four floats (exact).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
+  v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+// fp32 -> E4M3FN code, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t f32_to_fp8(float x) {
+  x = fminf(fmaxf(x, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xffu;
+}
+
+// ---------------------------------------------------------------- scores and keys
+
+// Projected score of one token before the scale: sum_i qhat_i * dec(code_i) in
+// fp32, as four FMA chains (chain e takes the elements i with i % 16 in
+// [4e, 4e+4)), summed (c0 + c1) + (c2 + c3).  Every kernel that scores a token
+// uses this function, so they all get the same bits.  R = scoring dims / 16;
+// `pc` holds the token's R 16-byte pieces.
+template <int R>
+__device__ __forceinline__ float score_pieces(const uint4 (&pc)[R], const float* qh) {
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const uint32_t w[4] = {pc[j].x, pc[j].y, pc[j].z, pc[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float f[4];
+      fp8x4_to_f32(w[e], f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[e] = __builtin_fmaf(f[i], qh[j * 16 + e * 4 + i], acc[e]);
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Order-preserving float -> uint32 map; -0 and +0 share one key.  Finite
+// scores map to keys >= 0x00800000, so key 0 is free to mean "no token".
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- lane utilities
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over each row of 16 lanes (DPP row rotations); every lane of the row
+// receives the row total.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0x128>(x);  // row_ror:8
+  x += dpp_f<0x124>(x);  // row_ror:4
+  x += dpp_f<0x122>(x);  // row_ror:2
+  x += dpp_f<0x121>(x);  // row_ror:1
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x |= (uint32_t)__shfl_xor((int)x, o);
+  return x;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = (uint32_t)__shfl_up((int)x, o);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+
+// Block-wide exclusive prefix sum of one uint32 per thread; `tmp` is LDS with
+// at least NT/64 + 1 words.  Returns the exclusive prefix; *total gets the sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* tmp, uint32_t* total) {
+  constexpr int NW = NT / 64;
+  const int l = lane_id(), w = (int)(threadIdx.x >> 6);
+  uint32_t inc = wave_incl_scan(x);
+  if (l == 63) tmp[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t v = (l < NW) ? tmp[l] : 0u;
+    uint32_t vi = wave_incl_scan(v);
+    if (l < NW) tmp[l] = vi - v;
+    if (l == NW - 1) tmp[NW] = vi;
+  }
+  __syncthreads();
+  uint32_t res = tmp[w] + inc - x;
+  *total = tmp[NW];
+  __syncthreads();
+  return res;
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_or(uint32_t x, uint32_t* tmp) {
+  constexpr int NW = NT / 64;
+  const int l = lane_id(), w = (int)(threadIdx.x >> 6);
+  x = wave_or(x);
+  if (l == 0) tmp[w] = x;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) r |= tmp[i];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace jssa

@@ -1,0 +1,81 @@
+// Internal interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jssa {
+
+constexpr int kCandCap = 16384;       // candidate slots per (sequence, KV head)
+constexpr int kSampleMax = 8192;      // sampled tokens per (sequence, KV head)
+constexpr int kMaxChunks = 4096;      // stream chunks per sequence the finish kernel can order
+constexpr int kMlaLatent = 512;
+constexpr int kMlaRope = 64;
+
+struct StoreArgs {
+  const uint16_t* k_new;
+  const int32_t* slot;
+  const float* M;
+  uint8_t* kp;
+  float* kp_scale;
+  int T, Hkv, P, d, r, S, mla;
+};
+
+struct SelectArgs {
+  const uint16_t* q;
+  const float* M;
+  const uint8_t* kp;
+  const float* kp_scale;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t* indices;
+  float* scores_out;
+  // workspace
+  float* qhat;          // [batch, Hkv, S]
+  uint32_t* tau;        // [batch, Hkv]
+  uint32_t* counter;    // [batch, Hkv]
+  int32_t* chunk_tab;   // [batch, Hkv, max_chunks, 2]  (base, count)
+  uint32_t* cand_key;   // [batch, Hkv, kCandCap]
+  int32_t* cand_idx;    // [batch, Hkv, kCandCap]
+  int batch, Hq, Hkv, d, P, max_pages, r, S, B, G, mla;
+  int cp;               // pages per stream chunk (multiple of 4)
+  int max_chunks;
+  int force_exact;
+};
+
+struct AttendArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* indices;  // NULL: dense positions [lo, N)
+  float* part_o;           // [batch, Hq, splits, dv]
+  float* part_ml;          // [batch, Hq, splits, 2]  (running max in log2 units, sum)
+  uint16_t* out;           // [batch, Hq, dv]
+  float* lse_out;          // [batch, Hq] or NULL
+  float sm_log2;           // sm_scale * log2(e)
+  int batch, Hq, Hkv, P, max_pages, B, G, window;
+  int splits, split_len;
+};
+
+struct CalibArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  float* gq;
+  float* gk;
+  float* xq;               // workspace: fp32 qbar rows [Hkv, T, dm]
+  float* xk;               // workspace: fp32 key rows  [Hkv, T, dm]
+  int T, Hq, Hkv, d, dm, G, mla;
+};
+
+hipError_t launch_store(const StoreArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, int stages, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_calib(const CalibArgs& a, hipStream_t s);
+
+// host: per-head top-r eigenvectors of the unit-trace-normalised moment sum
+int32_t basis_impl(int hkv, int n, int r, const float* gq, const float* gk, float* m_out);
+
+}  // namespace jssa

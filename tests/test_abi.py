@@ -1,0 +1,127 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, validates arguments before touching the device, and its host
+eigensolver (jssa_basis) matches the oracle's calibration."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+L = pytest.importorskip("long_context_decode_amd")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "jssa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(jssa_\w+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_status_strings():
+    for s in range(-5, 1):
+        assert L.status_string(s) and L.status_string(s) != "unknown status"
+    assert L.status_string(7) == "unknown status"
+
+
+def _shape(**kw):
+    base = dict(kind=0, batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                max_pages_per_seq=8192, rank=32, budget=2048, select_mode=0)
+    base.update(kw)
+    return L.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=30), -2), (dict(budget=0), -2), (dict(budget=5000), -2), (dict(batch=0), -2),
+    (dict(head_dim=64), -3), (dict(page_size=8), -3), (dict(rank=24), -3), (dict(rank=256, head_dim=256), -3),
+    (dict(num_q_heads=48), -3), (dict(kind=7), -3), (dict(select_mode=3), -2),
+    (dict(kind=1, num_kv_heads=2, num_q_heads=128, head_dim=576, rank=64), -3),
+    (dict(kind=1, num_kv_heads=1, num_q_heads=128, head_dim=576, rank=64, page_size=64), 0),
+])
+def test_shape_validation(kw, status):
+    n = ctypes.c_size_t()
+    st = L.raw_library().jssa_workspace_bytes(ctypes.byref(_shape(**kw)), ctypes.byref(n))
+    assert st == status
+
+
+def test_workspace_and_page_sizes():
+    s = _shape()
+    ws = L.workspace_bytes(s)
+    # candidates dominate: 64 (b,h) x 16384 x 8 bytes
+    assert 64 * 16384 * 8 < ws < 64 * 1024 * 1024
+    assert L.kp_page_bytes(s) == (8 * 16 * 32, 8 * 16)
+    m = _shape(kind=1, num_kv_heads=1, num_q_heads=128, head_dim=576, rank=64, page_size=64)
+    assert L.kp_page_bytes(m) == (64 * 128, 64)
+
+
+def test_entry_points_reject_before_launch():
+    """Errors come back from host validation; nothing touches the device (there is none here)."""
+    lib = L.raw_library()
+    s = _shape()
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    ref = ctypes.byref(s)
+    assert lib.jssa_select(ref, nul, fake, fake, fake, fake, fake, fake, nul, fake, 1 << 40, nul) == -1
+    assert lib.jssa_select(ref, fake, fake, fake, fake, fake, fake, fake, nul, fake, 16, nul) == -4
+    assert lib.jssa_attend(ref, fake, fake, fake, fake, fake, nul, 0.1, fake, nul, fake, 1 << 40, nul) == -1
+    assert lib.jssa_attend(ref, fake, fake, fake, fake, fake, fake, 0.1, fake, nul, fake, 16, nul) == -4
+    assert lib.jssa_full_decode(ref, fake, fake, fake, fake, fake, -1, 0.1, fake, nul, fake, 1 << 40, nul) == -2
+    assert lib.jssa_decode(ref, fake, fake, nul, fake, fake, fake, fake, fake, fake, fake, fake, 0.1, fake, nul,
+                           fake, 1 << 40, nul) == -1
+    assert lib.jssa_store(ref, nul, fake, 4, fake, fake, fake, nul) == -1
+    assert lib.jssa_store(ref, fake, fake, -1, fake, fake, fake, nul) == -2
+    assert lib.jssa_store(ref, nul, nul, 0, nul, nul, nul, nul) == 0          # T = 0: nothing to do
+    bad = _shape(head_dim=64)
+    assert lib.jssa_select(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, nul, fake, 1 << 40, nul) == -3
+    assert lib.jssa_calib_moments(ref, nul, fake, 4, fake, fake, fake, 1 << 30, nul) == -1
+    assert lib.jssa_calib_moments(ref, fake, fake, 4, fake, fake, fake, 8, nul) == -4
+
+
+def test_host_basis_matches_oracle_calibration():
+    """jssa_basis (C++ Householder + QL) spans the oracle's subspace (numpy eigh)."""
+    from oracle import calibrate as cal
+    from synth import WORKLOADS, make_gqa_calibration, bf16_bits
+    w = WORKLOADS["tiny"]
+    q, k = make_gqa_calibration(w, 0)
+    q64, k64 = cal.bf16_to_f64(bf16_bits(q)), cal.bf16_to_f64(bf16_bits(k))
+    gq, gk = cal.moments_per_head(q64, k64, w.group)
+    T = q64.shape[0]
+    m = L.jssa_basis(L.shape_for(w), (gq * T).astype(np.float32), (gk * T).astype(np.float32))
+    for h in range(w.num_kv_heads):
+        mo = cal.basis(gq[h], gk[h], w.rank)
+        mh = m[h].astype(np.float64)
+        assert np.abs(mh @ mh.T - np.eye(w.rank)).max() < 1e-5
+        # same projector (the eigengap keeps it well conditioned), same sign rule
+        assert np.abs(mh.T @ mh - mo.T @ mo).max() < 1e-3
+        assert abs(cal.l_marg(mh.T @ mh, gq[h], gk[h]) - cal.l_marg(mo.T @ mo, gq[h], gk[h])) < 1e-6
+        for row in mh:
+            assert row[np.argmax(np.abs(row))] > 0
+
+
+def test_host_basis_exact_on_known_spectrum():
+    """Diagonalisable input with a known eigenbasis: the rows come back exactly (up to fp32)."""
+    from synth.workloads import haar_orthogonal
+    d, r = 64, 16
+    u = haar_orthogonal(d, 3)
+    lam = np.linspace(2.0, 0.1, d)
+    a = (u * lam) @ u.T
+    s = L.make_shape(0, 1, 1, 1, 128, 16, 1, r, 16)
+    # head_dim must be a supported d; embed the 64-dim problem in 128 dims
+    big = np.zeros((128, 128))
+    big[:64, :64] = a
+    big[64:, 64:] = np.diag(np.linspace(0.05, 0.01, 64))
+    m = L.jssa_basis(s, big[None].astype(np.float32), big[None].astype(np.float32))[0]
+    for i in range(r):
+        v = u[:, i]
+        v = v * np.sign(v[np.argmax(np.abs(v))])
+        assert np.abs(m[i, :64] - v).max() < 1e-4 and np.abs(m[i, 64:]).max() < 1e-6
