@@ -23,19 +23,21 @@ struct Plan {
   int cp, max_chunks;
   int sp_splits, sp_len;     // sparse attention split plan
   int dn_splits, dn_len;     // dense (window 0) split plan
-  size_t off_qhat, off_tau, off_counter, off_chunk, off_ckey, off_cidx, off_part_o, off_part_ml, total;
+  size_t off_qhat, off_tau, off_chunk, off_ckey, off_cidx, off_part_o, off_part_ml, total;
 };
 
+// Split plan of the attention kernels: about 512 blocks of four wavefronts,
+// each wavefront taking whole batches of 64 positions.
 void split_plan(int64_t n_tok_max, int pairs, int* splits, int* len) {
   if (n_tok_max <= 0) {
     *splits = 1;
-    *len = 64;
+    *len = 256;
     return;
   }
-  int64_t s = cdiv(2048, std::max(pairs, 1));
-  s = std::min<int64_t>(s, cdiv(n_tok_max, 64));
+  int64_t s = cdiv(512, std::max(pairs, 1));
+  s = std::min<int64_t>(s, cdiv(n_tok_max, 256));
   s = std::max<int64_t>(1, std::min<int64_t>(s, 256));
-  int64_t l = cdiv(cdiv(n_tok_max, s), 64) * 64;
+  const int64_t l = cdiv(cdiv(n_tok_max, s), 256) * 256;
   *len = (int)l;
   *splits = (int)cdiv(n_tok_max, l);
 }
@@ -80,26 +82,21 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   p->G = p->Hq / p->Hkv;
   p->dv = p->mla ? kMlaLatent : p->d;
   p->maxN = (int64_t)p->max_pages * p->P;
-  // stream chunking: aim for >= 2048 blocks, chunk of 4..64 pages
-  const int hpw = 64 / p->P;
-  const int hg = (p->Hkv + hpw - 1) / hpw;
-  int cp = 64;
-  while (cp > 4 && (int64_t)p->batch * hg * cdiv(p->max_pages, cp) < 2048) cp /= 2;
-  while (cdiv(p->max_pages, cp) > kMaxChunks && cp < 64) cp *= 2;
-  if (cdiv(p->max_pages, cp) > kMaxChunks) return JSSA_ERR_UNSUPPORTED;
-  p->cp = cp;
-  p->max_chunks = (int)cdiv(p->max_pages, cp);
+  // stream chunking: one wavefront per chunk of 16 / (S / 16) pages
+  p->cp = std::max(1, 16 / (p->S / 16));
+  p->max_chunks = (int)cdiv(p->max_pages, p->cp);
+  if (p->max_chunks > kMaxChunks) return JSSA_ERR_UNSUPPORTED;
   split_plan(std::min<int64_t>(p->B, p->maxN), p->batch * p->Hkv, &p->sp_splits, &p->sp_len);
   split_plan(p->maxN, p->batch * p->Hkv, &p->dn_splits, &p->dn_len);
   const int max_splits = std::max(p->sp_splits, p->dn_splits);
   const size_t bh = (size_t)p->batch * p->Hkv;
+  const size_t cand = bh * p->max_chunks * p->cp * p->P;   // one region per stream chunk
   size_t off = 0;
   p->off_qhat = off;    off = align_up(off + bh * p->S * sizeof(float));
   p->off_tau = off;     off = align_up(off + bh * sizeof(uint32_t));
-  p->off_counter = off; off = align_up(off + bh * sizeof(uint32_t));
-  p->off_chunk = off;   off = align_up(off + bh * p->max_chunks * 2 * sizeof(int32_t));
-  p->off_ckey = off;    off = align_up(off + bh * kCandCap * sizeof(uint32_t));
-  p->off_cidx = off;    off = align_up(off + bh * kCandCap * sizeof(int32_t));
+  p->off_chunk = off;   off = align_up(off + bh * p->max_chunks * sizeof(int32_t));
+  p->off_ckey = off;    off = align_up(off + cand * sizeof(uint32_t));
+  p->off_cidx = off;    off = align_up(off + cand * sizeof(int32_t));
   const size_t pj = (size_t)p->batch * p->Hq * max_splits;
   p->off_part_o = off;  off = align_up(off + pj * p->dv * sizeof(float));
   p->off_part_ml = off; off = align_up(off + pj * 2 * sizeof(float));
@@ -137,7 +134,8 @@ int32_t do_store(const Plan& p, const uint16_t* k_new, const int32_t* slot, int3
 
 int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q, const float* M, const uint8_t* kp,
                   const float* kp_scale, const int32_t* block_table, const int32_t* seq_lens, int32_t* indices,
-                  float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                  float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream, const uint16_t* k_new = nullptr,
+                  const int32_t* slot_new = nullptr) {
   if (!q || !M || !kp || !kp_scale || !block_table || !seq_lens || !indices || !ws) return JSSA_ERR_NULL;
   if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
   SelectArgs a{};
@@ -151,8 +149,9 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
   a.scores_out = scores_out;
   a.qhat = at<float>(ws, p.off_qhat);
   a.tau = at<uint32_t>(ws, p.off_tau);
-  a.counter = at<uint32_t>(ws, p.off_counter);
-  a.chunk_tab = at<int32_t>(ws, p.off_chunk);
+  a.chunk_cnt = at<int32_t>(ws, p.off_chunk);
+  a.k_new = k_new;
+  a.slot_new = slot_new;
   a.cand_key = at<uint32_t>(ws, p.off_ckey);
   a.cand_idx = at<int32_t>(ws, p.off_cidx);
   a.batch = p.batch;
@@ -304,12 +303,9 @@ int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
   if (k_new && !slot_new) return JSSA_ERR_NULL;
   if (workspace_bytes < p.total) return JSSA_ERR_WORKSPACE;
   if (p.mla) return JSSA_ERR_UNSUPPORTED;
-  if (k_new) {
-    st = do_store(p, k_new, slot_new, p.batch, M, kp, kp_scale, stream);
-    if (st != JSSA_OK) return st;
-  }
-  st = do_select(p, shape->select_mode, JSSA_STAGE_ALL, q, M, kp, kp_scale, block_table, seq_lens, indices, nullptr, workspace,
-                 workspace_bytes, stream);
+  // the prologue of select stores the new token
+  st = do_select(p, shape->select_mode, JSSA_STAGE_ALL, q, M, kp, kp_scale, block_table, seq_lens, indices, nullptr,
+                 workspace, workspace_bytes, stream, k_new, k_new ? slot_new : nullptr);
   if (st != JSSA_OK) return st;
   return do_attend(p, q, k_cache, v_cache, block_table, seq_lens, indices, 0, sm_scale, out, lse_out, workspace,
                    workspace_bytes, stream);

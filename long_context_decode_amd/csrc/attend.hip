@@ -6,15 +6,23 @@
 // range (README page §3: the Full-KV baseline; §4 notes: sliding-window layers
 // keep dense attention).
 //
-// Block = (split, KV head, sequence), 4 wavefronts.  A wavefront takes 64
-// positions at a time: each lane resolves one position to its K/V row offset
-// through the block table, then rows of 16 lanes walk the 64 rows, four at a
-// time; a lane holds D/16 contiguous elements of K and V (one 16-byte load for
-// d = 128).  Each loaded row is used by all G query heads of the KV head.  The
-// online softmax runs in base 2 (logits pre-scaled by sm * log2 e); partials
-// (unnormalised o, running max, running sum) are merged across the rows of a
-// wave with lane shuffles, across waves in LDS, and across splits by
-// merge_kernel.
+// Block = (split, KV head, sequence), 4 wavefronts; a wavefront takes 64
+// positions at a time ("batch"), lane i resolving position i to its K/V row
+// through the block table.  Row r of 16 lanes handles positions 16r..16r+15,
+// one per iteration; a lane holds D/16 contiguous elements of the row (one
+// 16-byte load for d = 128).  Per batch:
+//   A. the K rows are requested in groups of 8, then q.k is formed with
+//      v_dot2_f32_bf16 on the bf16 pairs and summed over the row with DPP;
+//      every position's logit (base 2, scaled by sm * log2 e) lands in the
+//      lane that owns the position;
+//   B. one softmax update per batch: the wave max of the 64 logits, a single
+//      rescale of the running state, p = 2^(x - m) per lane;
+//   C. the V rows are requested in groups of 8 and o += p v, p broadcast along
+//      the row with a lane permute.
+// Each loaded row serves all G query heads of the KV head.  The running max is
+// uniform over the wavefront, so the rows' partial sums add directly; waves
+// merge in LDS, splits in merge_kernel.  DENSE instantiates the full-KV /
+// sliding-window baseline (positions [lo, N) instead of an index list).
 #include "common.h"
 #include "kernels.h"
 
@@ -25,32 +33,81 @@ namespace {
 constexpr int kAttendThreads = 256;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-__device__ __forceinline__ void online_update(float x, float& m, float& l, float* o, const float* v, int n) {
-  const float mn = fmaxf(m, x);
-  const float ms = (mn == -INFINITY) ? 0.0f : mn;
-  const float alpha = __builtin_amdgcn_exp2f(m - ms);
-  const float p = __builtin_amdgcn_exp2f(x - ms);
-  l = l * alpha + p;
-  for (int e = 0; e < n; ++e) o[e] = o[e] * alpha + p * v[e];
-  m = mn;
-}
-
-__device__ __forceinline__ void merge_state(float& m, float& l, float* o, float mo, float lo, const float* oo,
-                                            int n) {
-  const float mn = fmaxf(m, mo);
-  const float ms = (mn == -INFINITY) ? 0.0f : mn;
-  const float a = __builtin_amdgcn_exp2f(m - ms), b = __builtin_amdgcn_exp2f(mo - ms);
-  l = l * a + lo * b;
-  for (int e = 0; e < n; ++e) o[e] = o[e] * a + oo[e] * b;
-  m = mn;
-}
-
 }  // namespace
 
-template <int D, int G>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Combine the splits of every (sequence, query head): o = sum_s 2^(m_s - m*) o_s /
+// sum_s 2^(m_s - m*) l_s, lse = ln 2 * (m* + log2 sum_s 2^(m_s - m*) l_s).
+// One block per (query head, sequence); the (m_s, l_s) of all splits are read
+// once into LDS, then every thread combines its dims.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(AttendArgs a) {
+  __shared__ float wsplit[256];
+  __shared__ float lsum;
+  __shared__ float mmax;
+  const int j = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
+  int N = a.seq_lens[b];
+  const int cap = a.max_pages * a.P;
+  N = N < 0 ? 0 : (N > cap ? cap : N);
+  int n_tok;
+  if (a.indices) n_tok = N < a.B ? N : a.B;
+  else n_tok = (a.window > 0 && N > a.window) ? a.window : N;
+  const int ns = min(a.splits, (n_tok + a.split_len - 1) / a.split_len);
+  const int64_t pj0 = ((int64_t)b * a.Hq + j) * a.splits;
+  // splits <= 256: thread s holds split s
+  float ms_ = -INFINITY, ls_ = 0.0f;
+  if (tid < ns) {
+    ls_ = a.part_ml[(pj0 + tid) * 2 + 1];
+    ms_ = ls_ > 0.0f ? a.part_ml[(pj0 + tid) * 2] : -INFINITY;
+  }
+  float mm = wave_max(ms_);
+  if ((tid & 63) == 0) wsplit[tid >> 6] = mm;
+  __syncthreads();
+  if (tid == 0) {
+    float m4 = -INFINITY;
+    for (int i = 0; i < 4; ++i) m4 = fmaxf(m4, wsplit[i]);
+    mmax = m4;
+  }
+  __syncthreads();
+  mm = mmax;
+  const float msafe = (mm == -INFINITY) ? 0.0f : mm;
+  const float f = (tid < ns && ls_ > 0.0f) ? __builtin_amdgcn_exp2f(ms_ - msafe) : 0.0f;
+  __syncthreads();
+  wsplit[tid] = f;
+  float lw = ls_ * f;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o);
+  if (tid == 0) lsum = 0.0f;
+  __syncthreads();
+  if ((tid & 63) == 0) atomicAdd(&lsum, lw);
+  __syncthreads();
+  const float L = lsum;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  for (int dim = tid; dim < D; dim += 256) {
+    float acc = 0.0f;
+    for (int s = 0; s < ns; ++s) acc += a.part_o[(pj0 + s) * D + dim] * wsplit[s];
+    a.out[((int64_t)b * a.Hq + j) * D + dim] = f32_to_bf16(acc * inv);
+  }
+  if (tid == 0 && a.lse_out) a.lse_out[(int64_t)b * a.Hq + j] = L > 0.0f ? (mm + log2f(L)) * kLn2 : -INFINITY;
+}
+
+template <int D, int G, bool DENSE>
 __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
-  constexpr int EPL = D / 16;  // elements per lane
-  constexpr int NV = EPL / 8;  // 16-byte loads per lane per row
+  constexpr int EPL = D / 16;   // elements per lane
+  constexpr int NV = EPL / 8;   // 16-byte loads per lane per row
+  constexpr int NP = EPL / 2;   // bf16 pairs per lane per row
+  constexpr int GRP = 8 / NV;   // rows whose loads are in flight together (32 VGPRs)
   __shared__ float red_o[4][G][D];
   __shared__ float red_ml[4][G][2];
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -61,7 +118,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   const int cap = a.max_pages * a.P;
   N = N < 0 ? 0 : (N > cap ? cap : N);
   int lo = 0, n_tok;
-  if (a.indices) {
+  if (!DENSE) {
     n_tok = N < a.B ? N : a.B;
   } else {
     lo = (a.window > 0 && N > a.window) ? N - a.window : 0;
@@ -71,19 +128,18 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   if (i0 >= n_tok) return;
   const int i1 = min(i0 + a.split_len, n_tok);
 
-  float qf[G][EPL];
+  // query heads of this KV head as bf16 pairs (unscaled; the scale is applied to the row sums)
+  uint32_t qp[G][NP];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * D + c16 * EPL;
+    const uint16_t* q = a.q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * D + c16 * EPL;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qp + v * 8);
-      const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[g][v * 8 + 2 * e] = bf16_lo(ws[e]) * a.sm_log2;
-        qf[g][v * 8 + 2 * e + 1] = bf16_hi(ws[e]) * a.sm_log2;
-      }
+      const uint4 u = *reinterpret_cast<const uint4*>(q + v * 8);
+      qp[g][4 * v] = u.x;
+      qp[g][4 * v + 1] = u.y;
+      qp[g][4 * v + 2] = u.z;
+      qp[g][4 * v + 3] = u.w;
     }
   }
   float m[G], l[G], o[G][EPL];
@@ -95,77 +151,114 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
     for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
   }
 
-  const int64_t row_stride = (int64_t)a.Hkv * D;   // elements between consecutive slots
-  const int32_t* idx = a.indices ? a.indices + ((int64_t)b * a.Hkv + h) * a.B : nullptr;
+  const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive token slots
+  const uint16_t* kbase = a.k_cache + (int64_t)h * D + c16 * EPL;
+  const uint16_t* vbase = a.v_cache + (int64_t)h * D + c16 * EPL;
+  const int32_t* idx = DENSE ? nullptr : a.indices + ((int64_t)b * a.Hkv + h) * a.B;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
+  // lane -> slot index (physical page * P + slot) of position ii, or -1
+  auto slot_of = [&](int ii) -> int {
+    if (ii >= i1) return -1;
+    const int t = DENSE ? lo + ii : idx[ii];
+    return t >= 0 ? bt[t / a.P] * a.P + (t % a.P) : -1;
+  };
+  int ri = slot_of(i0 + w * 64 + lane);
   for (int base = i0 + w * 64; base < i1; base += 256) {
-    // lane -> one position of this batch of 64, resolved to its row offset
-    const int ii = base + lane;
-    int64_t off = -1;
-    if (ii < i1) {
-      const int t = idx ? idx[ii] : lo + ii;
-      if (t >= 0) off = ((int64_t)bt[t / a.P] * a.P + (t % a.P)) * row_stride + (int64_t)h * D;
-    }
-    const int cnt = min(64, i1 - base);
-    for (int it = 0; it < 16; it += 4) {
-      if (it * 4 >= cnt) break;
-      uint4 kr[4][NV], vr[4][NV];
-      bool ok[4];
+    // the next batch's slots are resolved while this batch is in flight
+    const int ri_next = slot_of(base + 256 + lane);
+    // ---- A: logits of the 64 positions (row r, iteration u -> position 16r + u)
+    float xs[G];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int src = (it + u) * 4 + row;
-        const int lo32 = __shfl((int)(off & 0xffffffff), src);
-        const int hi32 = __shfl((int)(off >> 32), src);
-        int64_t ro = ((int64_t)hi32 << 32) | (uint32_t)lo32;
-        ok[u] = src < cnt && ro >= 0;
-        if (!ok[u]) ro = 0;
-        const uint16_t* kp = a.k_cache + ro + c16 * EPL;
-        const uint16_t* vp = a.v_cache + ro + c16 * EPL;
+    for (int g = 0; g < G; ++g) xs[g] = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          kr[u][v] = *reinterpret_cast<const uint4*>(kp + v * 8);
-          vr[u][v] = *reinterpret_cast<const uint4*>(vp + v * 8);
-        }
+    for (int u0 = 0; u0 < 16; u0 += GRP) {
+      uint4 kr[GRP][NV];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int rr = __shfl(ri, (lane & 48) + u0 + u);
+        const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) kr[u][v] = *reinterpret_cast<const uint4*>(kbase + ro + v * 8);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float kf[EPL], vf[EPL];
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          const uint32_t kw[4] = {kr[u][v].x, kr[u][v].y, kr[u][v].z, kr[u][v].w};
-          const uint32_t vw[4] = {vr[u][v].x, vr[u][v].y, vr[u][v].z, vr[u][v].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kf[v * 8 + 2 * e] = bf16_lo(kw[e]);
-            kf[v * 8 + 2 * e + 1] = bf16_hi(kw[e]);
-            vf[v * 8 + 2 * e] = bf16_lo(vw[e]);
-            vf[v * 8 + 2 * e + 1] = bf16_hi(vw[e]);
-          }
-        }
+      for (int u = 0; u < GRP; ++u) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          float part = 0.0f;
+          float acc = 0.0f;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) part = __builtin_fmaf(qf[g][e], kf[e], part);
-          float x = row16_sum(part);
-          if (!ok[u]) x = -INFINITY;
-          online_update(x, m[g], l[g], o[g], vf, EPL);
+          for (int v = 0; v < NV; ++v) {
+            acc = dot2_bf16(kr[u][v].x, qp[g][4 * v], acc);
+            acc = dot2_bf16(kr[u][v].y, qp[g][4 * v + 1], acc);
+            acc = dot2_bf16(kr[u][v].z, qp[g][4 * v + 2], acc);
+            acc = dot2_bf16(kr[u][v].w, qp[g][4 * v + 3], acc);
+          }
+          const float x = row16_sum(acc) * a.sm_log2;
+          if (c16 == u0 + u) xs[g] = x;
         }
       }
     }
+    if (ri < 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) xs[g] = -INFINITY;
+    }
+    // ---- B: one softmax update for the batch
+    float p[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mn = fmaxf(m[g], wave_max(xs[g]));
+      if (mn > m[g]) {                     // uniform over the wavefront
+        const float al = __builtin_amdgcn_exp2f(m[g] - mn);
+        l[g] *= al;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] *= al;
+        m[g] = mn;
+      }
+      p[g] = (m[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(xs[g] - m[g]);
+      l[g] += p[g];
+    }
+    // ---- C: o += p v over the 64 rows
+#pragma unroll
+    for (int u0 = 0; u0 < 16; u0 += GRP) {
+      uint4 vr[GRP][NV];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int rr = __shfl(ri, (lane & 48) + u0 + u);
+        const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) vr[u][v] = *reinterpret_cast<const uint4*>(vbase + ro + v * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        float pp[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pp[g] = __shfl(p[g], (lane & 48) + u0 + u);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const uint32_t ww[4] = {vr[u][v].x, vr[u][v].y, vr[u][v].z, vr[u][v].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v0 = bf16_lo(ww[e]), v1 = bf16_hi(ww[e]);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              o[g][v * 8 + 2 * e] = __builtin_fmaf(pp[g], v0, o[g][v * 8 + 2 * e]);
+              o[g][v * 8 + 2 * e + 1] = __builtin_fmaf(pp[g], v1, o[g][v * 8 + 2 * e + 1]);
+            }
+          }
+        }
+      }
+    }
+    ri = ri_next;
   }
 
-  // merge the four rows of the wavefront (lanes c16, c16+16, c16+32, c16+48)
+  // rows share the wave's running max: sum the four rows and the lanes' l
 #pragma unroll
   for (int g = 0; g < G; ++g) {
+    l[g] = wave_sum(l[g]);
 #pragma unroll
-    for (int sh = 16; sh <= 32; sh <<= 1) {
-      float oo[EPL];
-      const float mo = __shfl_xor(m[g], sh), lo2 = __shfl_xor(l[g], sh);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) oo[e] = __shfl_xor(o[g][e], sh);
-      merge_state(m[g], l[g], o[g], mo, lo2, oo, EPL);
+    for (int e = 0; e < EPL; ++e) {
+      o[g][e] += __shfl_xor(o[g][e], 16);
+      o[g][e] += __shfl_xor(o[g][e], 32);
     }
     if (row == 0) {
 #pragma unroll
@@ -200,48 +293,17 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   }
 }
 
-// Combine the splits of every (sequence, query head): o = sum_s 2^(m_s - m*) o_s /
-// sum_s 2^(m_s - m*) l_s, lse = ln 2 * (m* + log2 sum_s 2^(m_s - m*) l_s).
-__global__ __launch_bounds__(256) void merge_kernel(AttendArgs a, int D) {
-  const int j = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
-  int N = a.seq_lens[b];
-  const int cap = a.max_pages * a.P;
-  N = N < 0 ? 0 : (N > cap ? cap : N);
-  int n_tok;
-  if (a.indices) n_tok = N < a.B ? N : a.B;
-  else n_tok = (a.window > 0 && N > a.window) ? a.window : N;
-  const int ns = min(a.splits, (n_tok + a.split_len - 1) / a.split_len);
-  const int64_t pj0 = ((int64_t)b * a.Hq + j) * a.splits;
-  float mm = -INFINITY;
-  for (int s = 0; s < ns; ++s)
-    if (a.part_ml[(pj0 + s) * 2 + 1] > 0.0f) mm = fmaxf(mm, a.part_ml[(pj0 + s) * 2]);
-  const float ms = (mm == -INFINITY) ? 0.0f : mm;
-  float L = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float ls = a.part_ml[(pj0 + s) * 2 + 1];
-    if (ls > 0.0f) L += ls * __builtin_amdgcn_exp2f(a.part_ml[(pj0 + s) * 2] - ms);
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  for (int dim = tid; dim < D; dim += 256) {
-    float acc = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float ls = a.part_ml[(pj0 + s) * 2 + 1];
-      if (ls > 0.0f) acc += a.part_o[(pj0 + s) * D + dim] * __builtin_amdgcn_exp2f(a.part_ml[(pj0 + s) * 2] - ms);
-    }
-    a.out[((int64_t)b * a.Hq + j) * D + dim] = f32_to_bf16(acc * inv);
-  }
-  if (tid == 0 && a.lse_out)
-    a.lse_out[(int64_t)b * a.Hq + j] = L > 0.0f ? (mm + __log2f(L)) * kLn2 : -INFINITY;
-}
-
 namespace {
 
 template <int D, int G>
 hipError_t launch_dg(const AttendArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attend_kernel<D, G>), dim3(a.splits, a.Hkv, a.batch), dim3(kAttendThreads), 0, s, a);
+  if (a.indices)
+    hipLaunchKernelGGL((attend_kernel<D, G, false>), dim3(a.splits, a.Hkv, a.batch), dim3(kAttendThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_kernel<D, G, true>), dim3(a.splits, a.Hkv, a.batch), dim3(kAttendThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.Hq, a.batch), dim3(256), 0, s, a, D);
+  hipLaunchKernelGGL(merge_kernel<D>, dim3(a.Hq, a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

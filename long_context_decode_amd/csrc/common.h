@@ -42,6 +42,35 @@ __device__ __forceinline__ uint32_t f32_to_fp8(float x) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xffu;
 }
 
+// ---------------------------------------------------------------- projection of a key row
+
+// y = sum_i m[i] * x[i] over din bf16 inputs (din % 8 == 0), one fp32 FMA
+// chain in index order.  jssa_store and the store fused into jssa_decode both
+// use it, so a key gets the same codes either way.
+__device__ __forceinline__ float project_row(const float* __restrict__ m, const uint16_t* __restrict__ x, int din) {
+  float acc = 0.0f;
+  for (int i = 0; i < din; i += 8) {
+    const uint4 kv = *reinterpret_cast<const uint4*>(x + i);
+    const float4 m0 = *reinterpret_cast<const float4*>(m + i);
+    const float4 m1 = *reinterpret_cast<const float4*>(m + i + 4);
+    acc = __builtin_fmaf(m0.x, bf16_lo(kv.x), acc);
+    acc = __builtin_fmaf(m0.y, bf16_hi(kv.x), acc);
+    acc = __builtin_fmaf(m0.z, bf16_lo(kv.y), acc);
+    acc = __builtin_fmaf(m0.w, bf16_hi(kv.y), acc);
+    acc = __builtin_fmaf(m1.x, bf16_lo(kv.z), acc);
+    acc = __builtin_fmaf(m1.y, bf16_hi(kv.z), acc);
+    acc = __builtin_fmaf(m1.z, bf16_lo(kv.w), acc);
+    acc = __builtin_fmaf(m1.w, bf16_hi(kv.w), acc);
+  }
+  return acc;
+}
+
+// Byte offset of element o of the projected key at (page, head, slot) in the
+// piece-major scoring cache [pages][Hkv][S/16][P][16].
+__device__ __forceinline__ int64_t kp_offset(int64_t page, int head, int slot, int o, int Hkv, int S, int P) {
+  return (page * Hkv + head) * ((int64_t)S * P) + (o >> 4) * (P * 16) + slot * 16 + (o & 15);
+}
+
 // ---------------------------------------------------------------- scores and keys
 
 // Projected score of one token before the scale: sum_i qhat_i * dec(code_i) in

@@ -34,12 +34,14 @@ struct SelectArgs {
   // workspace
   float* qhat;          // [batch, Hkv, S]
   uint32_t* tau;        // [batch, Hkv]
-  uint32_t* counter;    // [batch, Hkv]
-  int32_t* chunk_tab;   // [batch, Hkv, max_chunks, 2]  (base, count)
-  uint32_t* cand_key;   // [batch, Hkv, kCandCap]
-  int32_t* cand_idx;    // [batch, Hkv, kCandCap]
+  int32_t* chunk_cnt;   // [batch, Hkv, max_chunks] candidates found by each chunk
+  uint32_t* cand_key;   // [batch, Hkv, max_chunks, cp * P] (chunk regions)
+  int32_t* cand_idx;    // [batch, Hkv, max_chunks, cp * P]
+  // new-token store fused into the prologue (k_new == NULL: none)
+  const uint16_t* k_new;
+  const int32_t* slot_new;
   int batch, Hq, Hkv, d, P, max_pages, r, S, B, G, mla;
-  int cp;               // pages per stream chunk (multiple of 4)
+  int cp;               // pages per stream chunk (16 / (scoring dims / 16))
   int max_chunks;
   int force_exact;
 };

@@ -5,16 +5,18 @@
 //
 // Three launches on one stream:
 //  1. prologue  (one block per (sequence, KV head)): qbar = mean of the G query
-//     heads, qhat = M qbar (fp64, rounded once to fp32); scores a strided sample of the sequence's
-//     pages and picks a threshold key tau that about 4B tokens should clear
-//     (tau = "all" when the whole sequence fits the candidate buffer).
-//  2. stream    (blocks over (chunk of pages, group of KV heads, sequence)):
-//     every lane owns one (KV head, slot) of a page and reads that token's
-//     16-byte FP8 pieces (a wavefront reads one contiguous run per piece),
-//     computes its score and key into LDS; at the end of the chunk one wave
-//     per head compacts the keys >= tau, in position order, into the
-//     candidate buffer and records (base, count) for the chunk.
-//  3. finish    (one 1024-thread block per (sequence, KV head)): copies the
+//     heads, qhat = M qbar (fp64, rounded once to fp32); scores a strided
+//     sample of the sequence's pages and picks a threshold key tau that about
+//     2B tokens should clear (tau = "all" when the whole sequence fits the
+//     candidate buffer).  In jssa_decode it also stores the new token.
+//  2. stream    (each wavefront owns one chunk of 16/R consecutive pages of
+//     one sequence for a group of KV heads): every lane owns one (KV head,
+//     slot) and reads that token's 16-byte FP8 pieces for all pages of the
+//     chunk at once (a wavefront reads one contiguous run per piece), scores
+//     them, and the keys >= tau are compacted in position order straight from
+//     the ballot masks into the chunk's own region of the candidate buffer;
+//     the chunk's count is recorded.
+//  3. finish    (one 1024-thread block per (sequence, KV head)): gathers the
 //     candidates into LDS in chunk order (so they are in position order),
 //     radix-selects the B-th largest key, and writes the winners ascending
 //     with an ordered prefix-sum compaction (ties at the B-th key: lowest
@@ -29,39 +31,44 @@ namespace jssa {
 
 namespace {
 
-constexpr int kPrologueThreads = 256;
+constexpr int kPrologueThreads = 1024;
 constexpr int kFinishThreads = 1024;
 constexpr int kStreamThreads = 256;
-constexpr int kMaxCp = 64;             // pages per stream chunk, at most
 
 // ------------------------------------------------------------------ radix select
 
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
+
 // Pick the digit d of the current pass so that fewer than k matching keys have
-// a larger digit and at least k have a digit >= d.  Run by wave 0 only.
-__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t k, uint32_t* bcast) {
-  const int l = lane_id();
-  const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
-  const uint32_t s = c0 + c1 + c2 + c3;
-  uint32_t suf = s;  // inclusive suffix sum over lanes >= l
+// a larger digit and at least k have a digit >= d: thread t owns kBins/NT
+// consecutive bins; the count above its bins comes from a block prefix sum.
+template <int NT>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t k, uint32_t* tmp, uint32_t* bcast) {
+  constexpr int BPT = kBins / NT;
+  const int tid = (int)threadIdx.x;
+  uint32_t c[BPT], s = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t v = (uint32_t)__shfl_down((int)suf, o);
-    if (l + o < 64) suf += v;
+  for (int j = 0; j < BPT; ++j) {
+    c[j] = hist[tid * BPT + j];
+    s += c[j];
   }
-  uint32_t above = suf - s;
-  const uint32_t cs[4] = {c0, c1, c2, c3};
+  uint32_t total;
+  const uint32_t ex = block_excl_scan<NT>(s, tmp, &total);
+  uint32_t above = total - ex - s;  // keys in the bins of higher threads
 #pragma unroll
-  for (int j = 3; j >= 0; --j) {
-    if (above < k && k <= above + cs[j]) {
-      bcast[0] = (uint32_t)(4 * l + j);
+  for (int j = BPT - 1; j >= 0; --j) {
+    if (above < k && k <= above + c[j]) {
+      bcast[0] = (uint32_t)(tid * BPT + j);
       bcast[1] = k - above;
     }
-    above += cs[j];
+    above += c[j];
   }
 }
 
 // k-th largest key (1-based) of keys[0..n) held in LDS, and how many keys equal
-// to it belong to the top k.  Skips the leading bits that all keys share.
+// to it belong to the top k.  Skips the leading bits that all keys share, then
+// resolves kDigitBits bits per pass.
 template <int NT>
 __device__ void radix_select_lds(const uint32_t* keys, int n, uint32_t k, uint32_t* hist, uint32_t* tmp,
                                  uint32_t* kth, uint32_t* need) {
@@ -79,20 +86,20 @@ __device__ void radix_select_lds(const uint32_t* keys, int n, uint32_t k, uint32
   uint32_t hi_mask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
   uint32_t prefix = ref & hi_mask;
   while (true) {
-    const int shift = hb >= 7 ? hb - 7 : 0;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+    const int shift = hb >= kDigitBits - 1 ? hb - (kDigitBits - 1) : 0;
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
       const uint32_t key = keys[i];
-      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & (kBins - 1u)], 1u);
     }
     __syncthreads();
-    if (tid < 64) find_digit(hist, k, tmp + 32);
+    find_digit<NT>(hist, k, tmp, tmp + 48);
     __syncthreads();
-    const uint32_t d = tmp[32];
-    k = tmp[33];
+    const uint32_t d = tmp[48];
+    k = tmp[49];
+    prefix = (prefix & ~((kBins - 1u) << shift)) | (d << shift);
     hi_mask = ~((1u << shift) - 1u);
-    prefix = (prefix & ~(0xffu << shift)) | (d << shift);
     prefix &= hi_mask;
     __syncthreads();
     if (shift == 0) break;
@@ -135,72 +142,147 @@ __device__ __forceinline__ int seq_len_of(const SelectArgs& a, int b) {
 template <int R>
 __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a) {
   constexpr int S = R * 16;
+  constexpr int TPT = R >= 8 ? 1 : 8 / R;      // sampled tokens per thread with loads in flight together
   const int h = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
   __shared__ double qbar[kMlaLatent + kMlaRope];
   __shared__ float qh[S];
+  __shared__ float ynew[S];
   __shared__ uint32_t skeys[kSampleMax];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kBins];
   __shared__ uint32_t tmp[64];
+  const int64_t bh = (int64_t)b * a.Hkv + h;
   const int N = seq_len_of(a, b);
   const int din = a.mla ? kMlaLatent + kMlaRope : a.d;
+  const int dm = a.mla ? kMlaLatent : a.d;
+  const float* Mh = a.M + (int64_t)(a.mla ? 0 : h) * a.r * dm;
 
-  // qbar: mean of the G query heads of KV head h.  The projection runs in fp64
-  // and is rounded to fp32 once, so qhat carries one rounding.
+  // sample plan: a strided set of whole pages; tau will be the ks-th largest
+  // sampled key with ks / sample = target / N, target = min(2B, cap/2)
+  const bool sampled = !a.force_exact && N > kCandCap;
+  int sp = 0, n_pages = 0;
+  if (sampled) {
+    n_pages = (N + a.P - 1) / a.P;
+    int64_t want = (int64_t)64 * N / a.B;
+    if (want < 2048) want = 2048;
+    if (want > kSampleMax) want = kSampleMax;
+    sp = (int)((want + a.P - 1) / a.P);
+    if (sp > kSampleMax / a.P) sp = kSampleMax / a.P;
+    if (sp > n_pages) sp = n_pages;
+  }
+  const int ns = sp * a.P;
+  // first round of sample loads goes out before the query projection
+  uint4 pc[TPT][R];
+  float sc[TPT];
+  int tt[TPT];
+  auto issue = [&](int u0) {
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int u = u0 + j * kPrologueThreads + tid;
+      tt[j] = -1;
+      if (u < ns) {
+        const int i = u / a.P, slot = u % a.P;
+        const int pl = (int)(((int64_t)i * n_pages) / sp);
+        const int t = pl * a.P + slot;
+        if (t < N) {
+          tt[j] = t;
+          const int64_t phys = a.block_table[(int64_t)b * a.max_pages + pl];
+          load_token<R>(a, phys, h, slot, pc[j], sc[j]);
+        }
+      }
+    }
+  };
+  if (sampled) issue(0);
+
+  // qbar: mean of the G query heads of KV head h (fp64)
   for (int i = tid; i < din; i += kPrologueThreads) {
     double s = 0.0;
     const uint16_t* qp = a.q + ((int64_t)b * a.Hq + (int64_t)h * a.G) * din + i;
-    for (int g = 0; g < a.G; ++g) s += (double)bf16_to_f32(qp[(int64_t)g * din]);
+    for (int g0 = 0; g0 < a.G; g0 += 8) {      // eight heads' loads in flight, summed in head order
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = g0 + j < a.G ? bf16_to_f32(qp[(int64_t)(g0 + j) * din]) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += (double)v[j];
+    }
     qbar[i] = s / (double)a.G;
   }
+  // the new token of this sequence (jssa_decode): projected exactly as jssa_store does
+  const int new_slot = a.k_new ? a.slot_new[b] : -1;
+  if (new_slot >= 0 && tid < S) {
+    const uint16_t* row = a.mla ? a.k_new + (int64_t)b * din : a.k_new + ((int64_t)b * a.Hkv + h) * a.d;
+    ynew[tid] = tid < a.r ? project_row(Mh + (int64_t)tid * dm, row, dm) : bf16_to_f32(row[kMlaLatent + (tid - a.r)]);
+  }
   __syncthreads();
-  // qhat = M qbar (MLA: [M qbar[:512] ; qbar[512:]])
-  for (int o = tid; o < S; o += kPrologueThreads) {
-    double v;
+  // qhat = M qbar (MLA: [M qbar[:512] ; qbar[512:]]) in fp64, rounded once to
+  // fp32: 8 threads per output, each one eighth of the dims, fixed xor order
+  {
+    const int o = tid >> 3, part = tid & 7;
+    double v = 0.0;
     if (o < a.r) {
-      const int dm = a.mla ? kMlaLatent : a.d;
-      const float* m = a.M + ((int64_t)(a.mla ? 0 : h) * a.r + o) * dm;
-      double acc = 0.0;
-      for (int i = 0; i < dm; ++i) acc = __builtin_fma((double)m[i], qbar[i], acc);
-      v = acc;
-    } else {
-      v = qbar[kMlaLatent + (o - a.r)];
+      const int len = dm / 8;
+      const float* m = Mh + (int64_t)o * dm + part * len;
+      const double* qb = qbar + part * len;
+      for (int i = 0; i < len; i += 8) {
+        const float4 m0 = *reinterpret_cast<const float4*>(m + i);
+        const float4 m1 = *reinterpret_cast<const float4*>(m + i + 4);
+        v = __builtin_fma((double)m0.x, qb[i], v);
+        v = __builtin_fma((double)m0.y, qb[i + 1], v);
+        v = __builtin_fma((double)m0.z, qb[i + 2], v);
+        v = __builtin_fma((double)m0.w, qb[i + 3], v);
+        v = __builtin_fma((double)m1.x, qb[i + 4], v);
+        v = __builtin_fma((double)m1.y, qb[i + 5], v);
+        v = __builtin_fma((double)m1.z, qb[i + 6], v);
+        v = __builtin_fma((double)m1.w, qb[i + 7], v);
+      }
     }
-    qh[o] = (float)v;
-    a.qhat[((int64_t)b * a.Hkv + h) * S + o] = (float)v;
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    if (o < S && part == 0) {
+      if (o >= a.r) v = qbar[kMlaLatent + (o - a.r)];
+      qh[o] = (float)v;
+      a.qhat[bh * S + o] = (float)v;
+    }
+  }
+  if (new_slot >= 0 && tid < 64) {
+    float am = 0.0f;
+    for (int o = tid; o < S; o += 64) am = fmaxf(am, fabsf(ynew[o]));
+    am = wave_max(am);
+    const float scale = am / 448.0f;
+    const int page = new_slot / a.P, sip = new_slot % a.P;
+    for (int o = tid; o < S; o += 64) {
+      const uint32_t code = (scale > 0.0f) ? f32_to_fp8(ynew[o] / scale) : 0u;
+      const_cast<uint8_t*>(a.kp)[kp_offset(page, h, sip, o, a.Hkv, S, a.P)] = (uint8_t)code;
+    }
+    if (tid == 0) const_cast<float*>(a.kp_scale)[((int64_t)page * a.Hkv + h) * a.P + sip] = scale;
   }
   __syncthreads();
 
   uint32_t tau;
   if (a.force_exact) {
     tau = 0xffffffffu;                   // stream keeps nothing; finish runs the exact path
-  } else if (N <= kCandCap) {
+  } else if (!sampled) {
     tau = 0u;                            // every token is a candidate
   } else {
-    // strided page sample; tau = the ks-th largest sampled key with
-    // ks / sample = target / N, target = min(4B, cap/2) candidates
-    const int n_pages = (N + a.P - 1) / a.P;
-    int64_t want = (int64_t)32 * N / a.B;
-    if (want < 2048) want = 2048;
-    if (want > kSampleMax) want = kSampleMax;
-    int sp = (int)((want + a.P - 1) / a.P);
-    if (sp > kSampleMax / a.P) sp = kSampleMax / a.P;
-    if (sp > n_pages) sp = n_pages;
-    const int ns = sp * a.P;
     uint32_t valid = 0;
-    for (int u = tid; u < ns; u += kPrologueThreads) {
-      const int i = u / a.P, slot = u % a.P;
-      const int pl = (int)(((int64_t)i * n_pages) / sp);
-      const int t = pl * a.P + slot;
-      uint32_t key = 0u;
-      if (t < N) {
-        key = token_key<R>(a, b, h, t, qh);
-        ++valid;
+    for (int u0 = 0; u0 < ns; u0 += kPrologueThreads * TPT) {
+      if (u0 > 0) issue(u0);
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) {
+        const int u = u0 + j * kPrologueThreads + tid;
+        if (u < ns) {
+          uint32_t key = 0u;
+          if (tt[j] >= 0) {
+            key = score_key(score_pieces<R>(pc[j], qh) * sc[j]);
+            ++valid;
+          }
+          skeys[u] = key;
+        }
       }
-      skeys[u] = key;
     }
     uint32_t nvalid;
     (void)block_excl_scan<kPrologueThreads>(valid, tmp, &nvalid);
-    const int64_t target = (int64_t)(4 * a.B < kCandCap / 2 ? 4 * a.B : kCandCap / 2);
+    const int64_t target = (int64_t)(2 * a.B < kCandCap / 2 ? 2 * a.B : kCandCap / 2);
     int64_t ks = (nvalid * target + N - 1) / N;
     if (ks < 1) ks = 1;
     if (ks > (int64_t)nvalid) ks = nvalid;
@@ -208,10 +290,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     radix_select_lds<kPrologueThreads>(skeys, ns, (uint32_t)ks, hist, tmp, &kth, &need);
     tau = kth;
   }
-  if (tid == 0) {
-    a.tau[(int64_t)b * a.Hkv + h] = tau;
-    a.counter[(int64_t)b * a.Hkv + h] = 0u;
-  }
+  if (tid == 0) a.tau[bh] = tau;
 }
 
 // ================================================================== 2. stream
@@ -219,23 +298,33 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 template <int R, int P>
 __global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
   constexpr int S = R * 16;
-  constexpr int HPW = 64 / P;  // KV heads covered by one wavefront
-  __shared__ uint32_t keys[HPW][kMaxCp * P];
-  const int c = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  constexpr int HPW = 64 / P;               // KV heads covered by one wavefront
+  constexpr int PF = R >= 16 ? 1 : 16 / R;  // pages of a chunk (all in flight at once)
+  const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+  const int c = blockIdx.x * 4 + w, hg = blockIdx.y, b = blockIdx.z;
   const int N = seq_len_of(a, b);
   const int n_pages = (N + P - 1) / P;
-  const int page0 = c * a.cp;
+  const int page0 = c * PF;
   if (page0 >= n_pages) return;
-  const int pages_here = min(a.cp, n_pages - page0);
-  const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
   const int hl = lane / P, slot = lane % P;
   const int head = hg * HPW + hl;
   const bool active = head < a.Hkv;
   const int headc = active ? head : 0;
+  const int64_t bh = (int64_t)b * a.Hkv + headc;
 
+  // physical pages of the chunk: lane i < PF holds page page0 + i
+  int phys_l = 0;
+  if (lane < PF && page0 + lane < n_pages) phys_l = a.block_table[(int64_t)b * a.max_pages + page0 + lane];
+  uint4 pc[PF][R];
+  float sc[PF];
+#pragma unroll
+  for (int f = 0; f < PF; ++f) {
+    const int64_t phys = __builtin_amdgcn_readlane(phys_l, f);
+    if (active && page0 + f < n_pages) load_token<R>(a, phys, head, slot, pc[f], sc[f]);
+  }
   float qh[S];
   {
-    const float* src = a.qhat + ((int64_t)b * a.Hkv + headc) * S;
+    const float* src = a.qhat + bh * S;
 #pragma unroll
     for (int i = 0; i < S; i += 4) {
       const float4 v = *reinterpret_cast<const float4*>(src + i);
@@ -245,82 +334,43 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
       qh[i + 3] = v.w;
     }
   }
-
-  // this wave's pages: a contiguous run of the chunk, in order
-  const int per = a.cp / 4;
-  const int pb = w * per;
-  const int pe = min(pb + per, pages_here);
-  int phys_l = 0;
-  if (lane < per && pb + lane < pages_here)
-    phys_l = a.block_table[(int64_t)b * a.max_pages + page0 + pb + lane];
+  uint32_t tau = a.tau[bh];
+  if (tau == 0u) tau = 1u;                   // key 0 marks "no token"
   const int64_t maxN = (int64_t)a.max_pages * P;
-  float* sout = a.scores_out ? a.scores_out + ((int64_t)b * a.Hkv + headc) * maxN : nullptr;
+  float* sout = a.scores_out ? a.scores_out + bh * maxN : nullptr;
 
-  if (pb < pe) {
-    uint4 cur[R];
-    float csc = 0.0f;
-    {
-      const int64_t phys = __builtin_amdgcn_readlane(phys_l, 0);
-      if (active) load_token<R>(a, phys, head, slot, cur, csc);
-    }
-    for (int pi = pb; pi < pe; ++pi) {
-      uint4 nxt[R];
-      float nsc = 0.0f;
-      if (pi + 1 < pe) {
-        const int64_t phys = __builtin_amdgcn_readlane(phys_l, pi + 1 - pb);
-        if (active) load_token<R>(a, phys, head, slot, nxt, nsc);
-      }
-      const int t = (page0 + pi) * P + slot;
-      uint32_t key = 0u;
-      if (active && t < N) {
-        const float s = score_pieces<R>(cur, qh) * csc;
-        key = score_key(s);
-        if (sout) sout[t] = s;
-      }
-      keys[hl][pi * P + slot] = key;
+  // keys, flags and the ballot mask of every page of the chunk
+  uint32_t key[PF];
+  uint64_t mask[PF];
 #pragma unroll
-      for (int j = 0; j < R; ++j) cur[j] = nxt[j];
-      csc = nsc;
+  for (int f = 0; f < PF; ++f) {
+    const int t = (page0 + f) * P + slot;
+    key[f] = 0u;
+    if (active && t < N) {
+      const float s = score_pieces<R>(pc[f], qh) * sc[f];
+      key[f] = score_key(s);
+      if (sout) sout[t] = s;
     }
+    mask[f] = ballot(key[f] >= tau);
   }
-  __syncthreads();
-
-  // ordered compaction of keys >= tau, one wavefront per KV head
-  const int n = pages_here * P;
-  for (int h2 = w; h2 < HPW; h2 += 4) {
-    const int head2 = hg * HPW + h2;
-    if (head2 >= a.Hkv) break;
-    const int64_t bh = (int64_t)b * a.Hkv + head2;
-    uint32_t tau = a.tau[bh];
-    if (tau == 0u) tau = 1u;                         // key 0 marks "no token"
-    uint32_t cnt = 0;
-    for (int i0 = 0; i0 < n; i0 += 64) {
-      const int i = i0 + lane;
-      const bool f = i < n && keys[h2][i] >= tau;
-      cnt += (uint32_t)__popcll(ballot(f));
+  // per head: count of the chunk and its candidates, in position order, at the
+  // start of the chunk's own region of the candidate buffer (no atomics)
+  const uint64_t hmask = (P == 64) ? ~0ull : (((1ull << P) - 1ull) << (hl * P));
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int f = 0; f < PF; ++f) cnt += (uint32_t)__popcll(mask[f] & hmask);
+  const int64_t region = (bh * a.max_chunks + c) * (int64_t)(PF * P);
+  if (slot == 0 && active) a.chunk_cnt[bh * a.max_chunks + c] = (int32_t)cnt;
+  uint32_t run = 0;
+#pragma unroll
+  for (int f = 0; f < PF; ++f) {
+    const uint64_t m = mask[f] & hmask;
+    if (m & (1ull << lane)) {
+      const int64_t pos = region + run + lanes_below(m);
+      a.cand_key[pos] = key[f];
+      a.cand_idx[pos] = (page0 + f) * P + slot;
     }
-    uint32_t base = 0;
-    if (lane == 0) {
-      base = cnt ? atomicAdd(&a.counter[bh], cnt) : 0u;
-      int32_t* tab = a.chunk_tab + (bh * a.max_chunks + c) * 2;
-      tab[0] = (int32_t)base;
-      tab[1] = (int32_t)cnt;
-    }
-    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-    if (cnt == 0) continue;
-    uint32_t run = 0;
-    for (int i0 = 0; i0 < n; i0 += 64) {
-      const int i = i0 + lane;
-      const uint32_t key = i < n ? keys[h2][i] : 0u;
-      const bool f = i < n && key >= tau;
-      const uint64_t m = ballot(f);
-      const uint32_t pos = base + run + lanes_below(m);
-      if (f && pos < (uint32_t)kCandCap) {
-        a.cand_key[bh * kCandCap + pos] = key;
-        a.cand_idx[bh * kCandCap + pos] = page0 * P + i;
-      }
-      run += (uint32_t)__popcll(m);
-    }
+    run += (uint32_t)__popcll(m);
   }
 }
 
@@ -335,23 +385,25 @@ __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, in
                                     uint32_t* hist, uint32_t* tmp, int32_t* out) {
   const int tid = (int)threadIdx.x;
   uint32_t prefix = 0u, hi_mask = 0u, k = (uint32_t)K;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kFinishThreads) hist[i] = 0u;
+  for (int shift = 32 - kDigitBits; ; shift = shift > kDigitBits ? shift - kDigitBits : 0) {
+    for (int i = tid; i < kBins; i += kFinishThreads) hist[i] = 0u;
     __syncthreads();
     for (int t0 = 0; t0 < N; t0 += kFinishThreads) {
       const int t = t0 + tid;
       if (t < N) {
         const uint32_t key = token_key<R>(a, b, h, t, qh);
-        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & (kBins - 1u)], 1u);
       }
     }
     __syncthreads();
-    if (tid < 64) find_digit(hist, k, tmp + 32);
+    find_digit<kFinishThreads>(hist, k, tmp, tmp + 48);
     __syncthreads();
-    prefix |= tmp[32] << shift;
-    k = tmp[33];
-    hi_mask |= 0xffu << shift;
+    prefix = (prefix & ~((kBins - 1u) << shift)) | (tmp[48] << shift);
+    k = tmp[49];
+    hi_mask = ~((1u << shift) - 1u);
+    prefix &= hi_mask;
     __syncthreads();
+    if (shift == 0) break;
   }
   const uint32_t kth = prefix, need = k;
   uint32_t gt_run = 0, eq_run = 0;
@@ -378,8 +430,8 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
   __shared__ uint32_t lkey[kCandCap];
   __shared__ int32_t lidx[kCandCap];
-  __shared__ uint32_t coff[kMaxChunks];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t coff[kMaxChunks + 1];
+  __shared__ uint32_t hist[kBins];
   __shared__ uint32_t tmp[64];
   __shared__ float qh[S];
   const int64_t bh = (int64_t)b * a.Hkv + h;
@@ -389,39 +441,62 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   for (int i = K + tid; i < a.B; i += kFinishThreads) out[i] = -1;
   if (K == 0) return;
 
-  const uint32_t total = a.counter[bh];
   const uint32_t tau = a.tau[bh];
   const int n_pages = (N + a.P - 1) / a.P;
   const int n_chunks = (n_pages + a.cp - 1) / a.cp;
+  // chunk offsets in chunk (= position) order
+  const int32_t* cnts = a.chunk_cnt + bh * a.max_chunks;
+  uint32_t carry = 0;
+  for (int c0 = 0; c0 < n_chunks && !a.force_exact; c0 += kFinishThreads) {
+    const int c = c0 + tid;
+    const uint32_t cnt = c < n_chunks ? (uint32_t)cnts[c] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kFinishThreads>(cnt, tmp, &tot);
+    if (c < n_chunks) coff[c] = carry + ex;
+    carry += tot;
+  }
+  const uint32_t total = carry;
   const bool ok = !a.force_exact && total <= (uint32_t)kCandCap && total >= (uint32_t)K &&
-                  n_chunks <= kMaxChunks && (tau != 0u || total == (uint32_t)N);
+                  (tau != 0u || total == (uint32_t)N);
   if (!ok) {
     for (int i = tid; i < S; i += kFinishThreads) qh[i] = a.qhat[bh * S + i];
     __syncthreads();
     exact_stream_select<R>(a, b, h, N, K, qh, hist, tmp, out);
     return;
   }
-
-  // chunk offsets in chunk (= position) order
-  const int32_t* tab = a.chunk_tab + bh * a.max_chunks * 2;
-  uint32_t carry = 0;
-  for (int c0 = 0; c0 < n_chunks; c0 += kFinishThreads) {
-    const int c = c0 + tid;
-    const uint32_t cnt = c < n_chunks ? (uint32_t)tab[2 * c + 1] : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<kFinishThreads>(cnt, tmp, &tot);
-    if (c < n_chunks) coff[c] = carry + ex;
-    carry += tot;
-  }
+  if (tid == 0) coff[n_chunks] = carry;
   __syncthreads();
-  // copy candidates: one wavefront per chunk
-  const int lane = lane_id(), w = tid >> 6;
-  for (int c = w; c < n_chunks; c += kFinishThreads / 64) {
-    const int base = tab[2 * c], cnt = tab[2 * c + 1];
-    const uint32_t dst = coff[c];
-    for (int i = lane; i < cnt; i += 64) {
-      lkey[dst + i] = a.cand_key[bh * kCandCap + base + i];
-      lidx[dst + i] = a.cand_idx[bh * kCandCap + base + i];
+  // gather the candidates in position order: thread owns E consecutive slots
+  {
+    const int cap_chunk = a.cp * a.P;
+    const int per = ((int)total + kFinishThreads - 1) / kFinishThreads;
+    const int p0 = tid * per;
+    int lo = 0, hi = n_chunks;                   // last chunk with coff <= p0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (coff[mid] <= (uint32_t)p0) lo = mid;
+      else hi = mid;
+    }
+    int c = lo;
+    uint32_t kk[E];
+    int32_t ii[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int p = p0 + j;
+      if (j < per && p < (int)total) {
+        while (coff[c + 1] <= (uint32_t)p) ++c;
+        const int64_t src = (bh * a.max_chunks + c) * (int64_t)cap_chunk + (p - (int)coff[c]);
+        kk[j] = a.cand_key[src];
+        ii[j] = a.cand_idx[src];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int p = p0 + j;
+      if (j < per && p < (int)total) {
+        lkey[p] = kk[j];
+        lidx[p] = ii[j];
+      }
     }
   }
   __syncthreads();
@@ -454,7 +529,6 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
       ++eb;
     }
   }
-  (void)E;
 }
 
 // ================================================================== launch
@@ -471,7 +545,8 @@ hipError_t launch_select_rp(const SelectArgs& a, int stages, hipStream_t s) {
   }
   if (stages & 2) {
     const int hg = (a.Hkv + HPW - 1) / HPW;
-    hipLaunchKernelGGL((select_stream<R, P>), dim3(a.max_chunks, hg, a.batch), dim3(kStreamThreads), 0, s, a);
+    hipLaunchKernelGGL((select_stream<R, P>), dim3((a.max_chunks + 3) / 4, hg, a.batch), dim3(kStreamThreads), 0,
+                       s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4) {

@@ -30,22 +30,7 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
   for (int k = 0; k < 2; ++k) {
     const int o = lane + 64 * k;
     if (o < a.r) {
-      const float* m = a.M + ((int64_t)(a.mla ? 0 : h) * a.r + o) * din;
-      float acc = 0.0f;
-      for (int i = 0; i < din; i += 8) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(row + i);
-        const float4 m0 = *reinterpret_cast<const float4*>(m + i);
-        const float4 m1 = *reinterpret_cast<const float4*>(m + i + 4);
-        acc = __builtin_fmaf(m0.x, bf16_lo(kv.x), acc);
-        acc = __builtin_fmaf(m0.y, bf16_hi(kv.x), acc);
-        acc = __builtin_fmaf(m0.z, bf16_lo(kv.y), acc);
-        acc = __builtin_fmaf(m0.w, bf16_hi(kv.y), acc);
-        acc = __builtin_fmaf(m1.x, bf16_lo(kv.z), acc);
-        acc = __builtin_fmaf(m1.y, bf16_hi(kv.z), acc);
-        acc = __builtin_fmaf(m1.z, bf16_lo(kv.w), acc);
-        acc = __builtin_fmaf(m1.w, bf16_hi(kv.w), acc);
-      }
-      y[k] = acc;
+      y[k] = project_row(a.M + ((int64_t)(a.mla ? 0 : h) * a.r + o) * din, row, din);
     } else if (a.mla && o < a.S) {
       y[k] = bf16_to_f32(row[kMlaLatent + (o - a.r)]);   // RoPE dims pass through
     }
@@ -57,17 +42,15 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
   amax = wave_max(amax);
   const float scale = amax / 448.0f;
 
-  const int64_t blk = ((int64_t)page * a.Hkv + h);
-  uint8_t* dst = a.kp + blk * ((int64_t)a.S * a.P) + sip * 16;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int o = lane + 64 * k;
     if (o < a.S) {
       const uint32_t code = (scale > 0.0f) ? f32_to_fp8(y[k] / scale) : 0u;
-      dst[(o >> 4) * (a.P * 16) + (o & 15)] = (uint8_t)code;
+      a.kp[kp_offset(page, h, sip, o, a.Hkv, a.S, a.P)] = (uint8_t)code;
     }
   }
-  if (lane == 0) a.kp_scale[blk * a.P + sip] = scale;
+  if (lane == 0) a.kp_scale[((int64_t)page * a.Hkv + h) * a.P + sip] = scale;
 }
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
