@@ -54,10 +54,10 @@ class Shape(ctypes.Structure):
         return MLA_LATENT if self.kind == KIND_MLA else self.head_dim
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     S = ctypes.POINTER(Shape)
     sig = {

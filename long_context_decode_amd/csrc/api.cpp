@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <cstring>
 
-#include "../../include/jssa.h"
+#include "jssa.h"
 #include "kernels.h"
 
 namespace jssa {
@@ -23,7 +23,7 @@ struct Plan {
   int cp, max_chunks;
   int sp_splits, sp_len;     // sparse attention split plan
   int dn_splits, dn_len;     // dense (window 0) split plan
-  size_t off_qhat, off_tau, off_chunk, off_ckey, off_cidx, off_part_o, off_part_ml, total;
+  size_t off_qhat, off_tau, off_chunk, off_cand, off_part_o, off_part_ml, total;
 };
 
 // Split plan of the attention kernels: about 512 blocks of four wavefronts,
@@ -95,8 +95,7 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   p->off_qhat = off;    off = align_up(off + bh * p->S * sizeof(float));
   p->off_tau = off;     off = align_up(off + bh * sizeof(uint32_t));
   p->off_chunk = off;   off = align_up(off + bh * p->max_chunks * sizeof(int32_t));
-  p->off_ckey = off;    off = align_up(off + cand * sizeof(uint32_t));
-  p->off_cidx = off;    off = align_up(off + cand * sizeof(int32_t));
+  p->off_cand = off;    off = align_up(off + cand * 2 * sizeof(uint32_t));
   const size_t pj = (size_t)p->batch * p->Hq * max_splits;
   p->off_part_o = off;  off = align_up(off + pj * p->dv * sizeof(float));
   p->off_part_ml = off; off = align_up(off + pj * 2 * sizeof(float));
@@ -152,8 +151,7 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
   a.chunk_cnt = at<int32_t>(ws, p.off_chunk);
   a.k_new = k_new;
   a.slot_new = slot_new;
-  a.cand_key = at<uint32_t>(ws, p.off_ckey);
-  a.cand_idx = at<int32_t>(ws, p.off_cidx);
+  a.cand = at<uint2>(ws, p.off_cand);
   a.batch = p.batch;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;

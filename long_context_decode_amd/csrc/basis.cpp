@@ -12,7 +12,7 @@
 #include <numeric>
 #include <vector>
 
-#include "../../include/jssa.h"
+#include "jssa.h"
 
 namespace jssa {
 

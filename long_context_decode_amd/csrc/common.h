@@ -141,14 +141,23 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
   return x;
 }
 
-// Inclusive prefix sum over the wave.
+// x from the lane `CTRL` selects (DPP), 0 where the control has no source lane
+// or the row is masked off.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the wave with DPP: row shifts 1, 2, 4, 8 within
+// each row of 16 lanes, then row_bcast:15 and row_bcast:31 carry the row
+// totals across rows.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = (uint32_t)__shfl_up((int)x, o);
-    if (l >= o) x += y;
-  }
+  x += dpp_u<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_u<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_u<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_u<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_u<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_u<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 

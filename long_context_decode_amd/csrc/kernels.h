@@ -7,7 +7,7 @@
 
 namespace jssa {
 
-constexpr int kCandCap = 16384;       // candidate slots per (sequence, KV head)
+constexpr int kCandCap = 12288;       // candidates the finish kernel holds in LDS per (sequence, KV head)
 constexpr int kSampleMax = 8192;      // sampled tokens per (sequence, KV head)
 constexpr int kMaxChunks = 4096;      // stream chunks per sequence the finish kernel can order
 constexpr int kMlaLatent = 512;
@@ -35,8 +35,7 @@ struct SelectArgs {
   float* qhat;          // [batch, Hkv, S]
   uint32_t* tau;        // [batch, Hkv]
   int32_t* chunk_cnt;   // [batch, Hkv, max_chunks] candidates found by each chunk
-  uint32_t* cand_key;   // [batch, Hkv, max_chunks, cp * P] (chunk regions)
-  int32_t* cand_idx;    // [batch, Hkv, max_chunks, cp * P]
+  uint2* cand;          // [batch, Hkv, max_chunks, cp * P] (key, position), one region per chunk
   // new-token store fused into the prologue (k_new == NULL: none)
   const uint16_t* k_new;
   const int32_t* slot_new;

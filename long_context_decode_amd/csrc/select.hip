@@ -40,9 +40,17 @@ constexpr int kStreamThreads = 256;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 
+// Histogram bins are stored transposed with one word of padding per row: bin d
+// at word (d % 32) * 65 + d / 32.  Lane l of a wavefront then reads "its" 32
+// consecutive bins [32l, 32l + 32) with reads that are consecutive across
+// lanes, and neighbouring bins (where keys cluster) sit in different banks.
+constexpr int kHistWords = 32 * 65;
+__device__ __forceinline__ uint32_t bin_slot(uint32_t d) { return (d & 31u) * 65u + (d >> 5); }
+
 // Pick the digit d of the current pass so that fewer than k matching keys have
 // a larger digit and at least k have a digit >= d: thread t owns kBins/NT
 // consecutive bins; the count above its bins comes from a block prefix sum.
+// (Used by the exact re-scoring path, where the whole block streams tokens.)
 template <int NT>
 __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t k, uint32_t* tmp, uint32_t* bcast) {
   constexpr int BPT = kBins / NT;
@@ -50,7 +58,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t k, uin
   uint32_t c[BPT], s = 0;
 #pragma unroll
   for (int j = 0; j < BPT; ++j) {
-    c[j] = hist[tid * BPT + j];
+    c[j] = hist[bin_slot((uint32_t)(tid * BPT + j))];
     s += c[j];
   }
   uint32_t total;
@@ -66,17 +74,48 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t k, uin
   }
 }
 
-// k-th largest key (1-based) of keys[0..n) held in LDS, and how many keys equal
-// to it belong to the top k.  Skips the leading bits that all keys share, then
-// resolves kDigitBits bits per pass.
+
+// Wave 0 only: find the digit d with count(digit > d) < k <= count(digit >= d)
+// and publish d and k - count(digit > d) in bcast[0..1].
+__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k, uint32_t* bcast) {
+  const int l = lane_id();
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) sum += hist[j * 65 + l];
+  const uint32_t pre = wave_incl_scan(sum);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63);
+  const uint32_t suf = total - pre + sum;  // inclusive suffix sum over lanes >= l
+  const uint32_t above = suf - sum;
+  // the lane whose 32 bins hold the k-th key, then the bin among those 32,
+  // with lanes 0..31 taking one bin each (uniform control flow)
+  const int ls = (int)__builtin_ctzll(ballot(above < k && k <= suf));
+  const uint32_t above_ls = (uint32_t)__builtin_amdgcn_readlane((int)above, ls);
+  const uint32_t tot_ls = (uint32_t)__builtin_amdgcn_readlane((int)sum, ls);
+  const uint32_t cj = l < 32 ? hist[l * 65 + ls] : 0u;
+  const uint32_t pj = wave_incl_scan(cj);
+  const uint32_t incl = above_ls + (tot_ls - pj + cj), excl = incl - cj;
+  const bool hit = l < 32 && excl < k && k <= incl;
+  const int js = (int)__builtin_ctzll(ballot(hit));
+  if (l == js) {
+    bcast[0] = (uint32_t)(ls * 32 + js);
+    bcast[1] = k - excl;
+  }
+}
+
+// k-th largest key (1-based) of keys[0..n) in LDS and how many keys equal to it
+// belong to the top k.  Skips the leading bits all keys share, then resolves
+// kDigitBits bits per pass: every thread adds its keys to an LDS histogram,
+// wave 0 finds the digit; two block barriers per pass (the histogram of the
+// next pass is cleared during the current one).  hist2 holds 2 * kHistWords words.
 template <int NT>
-__device__ void radix_select_lds(const uint32_t* keys, int n, uint32_t k, uint32_t* hist, uint32_t* tmp,
-                                 uint32_t* kth, uint32_t* need) {
+__device__ void block_radix_select(const uint32_t* keys, int n, uint32_t k, uint32_t* hist2, uint32_t* tmp,
+                                   uint32_t* kth, uint32_t* need) {
   const int tid = (int)threadIdx.x;
+  for (int i = tid; i < kHistWords; i += NT) hist2[i] = 0u;
   const uint32_t ref = keys[0];
   uint32_t orv = 0;
   for (int i = tid; i < n; i += NT) orv |= keys[i] ^ ref;
-  orv = block_or<NT>(orv, tmp);
+  orv = block_or<NT>(orv, tmp);       // barriers also publish the cleared histogram
   if (orv == 0u) {
     *kth = ref;
     *need = k;
@@ -85,28 +124,28 @@ __device__ void radix_select_lds(const uint32_t* keys, int n, uint32_t k, uint32
   int hb = 31 - __builtin_clz(orv);
   uint32_t hi_mask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
   uint32_t prefix = ref & hi_mask;
-  while (true) {
+  for (int pass = 0;; ++pass) {
+    uint32_t* cur = hist2 + (pass & 1) * kHistWords;
+    uint32_t* nxt = hist2 + ((pass + 1) & 1) * kHistWords;
     const int shift = hb >= kDigitBits - 1 ? hb - (kDigitBits - 1) : 0;
-    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
-    __syncthreads();
     for (int i = tid; i < n; i += NT) {
       const uint32_t key = keys[i];
-      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & (kBins - 1u)], 1u);
+      if ((key & hi_mask) == prefix) atomicAdd(&cur[bin_slot((key >> shift) & (kBins - 1u))], 1u);
     }
+    for (int i = tid; i < kHistWords; i += NT) nxt[i] = 0u;
     __syncthreads();
-    find_digit<NT>(hist, k, tmp, tmp + 48);
+    if (tid < 64) wave_find_digit(cur, k, tmp + 48);
     __syncthreads();
-    const uint32_t d = tmp[48];
+    prefix = (prefix & ~((kBins - 1u) << shift)) | (tmp[48] << shift);
     k = tmp[49];
-    prefix = (prefix & ~((kBins - 1u) << shift)) | (d << shift);
     hi_mask = ~((1u << shift) - 1u);
     prefix &= hi_mask;
-    __syncthreads();
     if (shift == 0) break;
     hb = shift - 1;
   }
   *kth = prefix;
   *need = k;
+  __syncthreads();                     // tmp is reused by the caller
 }
 
 // ------------------------------------------------------------------ token access
@@ -148,7 +187,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   __shared__ float qh[S];
   __shared__ float ynew[S];
   __shared__ uint32_t skeys[kSampleMax];
-  __shared__ uint32_t hist[kBins];
+  __shared__ __align__(16) uint32_t hist[2 * kHistWords];
   __shared__ uint32_t tmp[64];
   const int64_t bh = (int64_t)b * a.Hkv + h;
   const int N = seq_len_of(a, b);
@@ -170,11 +209,13 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     if (sp > n_pages) sp = n_pages;
   }
   const int ns = sp * a.P;
-  // first round of sample loads goes out before the query projection
+  // sample loads go out in two steps around the query work: the block-table
+  // entries first (with the query loads), the FP8 rows before the projection
   uint4 pc[TPT][R];
   float sc[TPT];
   int tt[TPT];
-  auto issue = [&](int u0) {
+  int64_t ph[TPT];
+  auto issue_pages = [&](int u0) {
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
       const int u = u0 + j * kPrologueThreads + tid;
@@ -185,13 +226,17 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
         const int t = pl * a.P + slot;
         if (t < N) {
           tt[j] = t;
-          const int64_t phys = a.block_table[(int64_t)b * a.max_pages + pl];
-          load_token<R>(a, phys, h, slot, pc[j], sc[j]);
+          ph[j] = a.block_table[(int64_t)b * a.max_pages + pl];
         }
       }
     }
   };
-  if (sampled) issue(0);
+  auto issue_rows = [&]() {
+#pragma unroll
+    for (int j = 0; j < TPT; ++j)
+      if (tt[j] >= 0) load_token<R>(a, ph[j], h, tt[j] % a.P, pc[j], sc[j]);
+  };
+  if (sampled) issue_pages(0);
 
   // qbar: mean of the G query heads of KV head h (fp64)
   for (int i = tid; i < din; i += kPrologueThreads) {
@@ -206,6 +251,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     }
     qbar[i] = s / (double)a.G;
   }
+  if (sampled) issue_rows();
   // the new token of this sequence (jssa_decode): projected exactly as jssa_store does
   const int new_slot = a.k_new ? a.slot_new[b] : -1;
   if (new_slot >= 0 && tid < S) {
@@ -266,7 +312,10 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   } else {
     uint32_t valid = 0;
     for (int u0 = 0; u0 < ns; u0 += kPrologueThreads * TPT) {
-      if (u0 > 0) issue(u0);
+      if (u0 > 0) {
+        issue_pages(u0);
+        issue_rows();
+      }
 #pragma unroll
       for (int j = 0; j < TPT; ++j) {
         const int u = u0 + j * kPrologueThreads + tid;
@@ -287,7 +336,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     if (ks < 1) ks = 1;
     if (ks > (int64_t)nvalid) ks = nvalid;
     uint32_t kth, need;
-    radix_select_lds<kPrologueThreads>(skeys, ns, (uint32_t)ks, hist, tmp, &kth, &need);
+    block_radix_select<kPrologueThreads>(skeys, ns, (uint32_t)ks, hist, tmp, &kth, &need);
     tau = kth;
   }
   if (tid == 0) a.tau[bh] = tau;
@@ -355,7 +404,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
   }
   // per head: count of the chunk and its candidates, in position order, at the
   // start of the chunk's own region of the candidate buffer (no atomics)
-  const uint64_t hmask = (P == 64) ? ~0ull : (((1ull << P) - 1ull) << (hl * P));
+  const uint64_t hmask = (P == 64) ? ~0ull : (((1ull << (P & 63)) - 1ull) << (hl * P));
   uint32_t cnt = 0;
 #pragma unroll
   for (int f = 0; f < PF; ++f) cnt += (uint32_t)__popcll(mask[f] & hmask);
@@ -367,8 +416,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
     const uint64_t m = mask[f] & hmask;
     if (m & (1ull << lane)) {
       const int64_t pos = region + run + lanes_below(m);
-      a.cand_key[pos] = key[f];
-      a.cand_idx[pos] = (page0 + f) * P + slot;
+      a.cand[pos] = make_uint2(key[f], (uint32_t)((page0 + f) * P + slot));
     }
     run += (uint32_t)__popcll(m);
   }
@@ -386,13 +434,13 @@ __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, in
   const int tid = (int)threadIdx.x;
   uint32_t prefix = 0u, hi_mask = 0u, k = (uint32_t)K;
   for (int shift = 32 - kDigitBits; ; shift = shift > kDigitBits ? shift - kDigitBits : 0) {
-    for (int i = tid; i < kBins; i += kFinishThreads) hist[i] = 0u;
+    for (int i = tid; i < kHistWords; i += kFinishThreads) hist[i] = 0u;
     __syncthreads();
     for (int t0 = 0; t0 < N; t0 += kFinishThreads) {
       const int t = t0 + tid;
       if (t < N) {
         const uint32_t key = token_key<R>(a, b, h, t, qh);
-        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & (kBins - 1u)], 1u);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[bin_slot((key >> shift) & (kBins - 1u))], 1u);
       }
     }
     __syncthreads();
@@ -426,12 +474,11 @@ __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, in
 template <int R>
 __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   constexpr int S = R * 16;
-  constexpr int E = kCandCap / kFinishThreads;
   const int h = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
   __shared__ uint32_t lkey[kCandCap];
   __shared__ int32_t lidx[kCandCap];
   __shared__ uint32_t coff[kMaxChunks + 1];
-  __shared__ uint32_t hist[kBins];
+  __shared__ __align__(16) uint32_t hist[2 * kHistWords];
   __shared__ uint32_t tmp[64];
   __shared__ float qh[S];
   const int64_t bh = (int64_t)b * a.Hkv + h;
@@ -466,36 +513,33 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   }
   if (tid == 0) coff[n_chunks] = carry;
   __syncthreads();
-  // gather the candidates in position order: thread owns E consecutive slots
+  // gather the candidates in position order: thread c copies chunk c's
+  // contiguous run to its offset; the first 8 entries are read unconditionally
+  // (a region holds at least 32), the rest, if any, one by one
   {
     const int cap_chunk = a.cp * a.P;
-    const int per = ((int)total + kFinishThreads - 1) / kFinishThreads;
-    const int p0 = tid * per;
-    int lo = 0, hi = n_chunks;                   // last chunk with coff <= p0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (coff[mid] <= (uint32_t)p0) lo = mid;
-      else hi = mid;
-    }
-    int c = lo;
-    uint32_t kk[E];
-    int32_t ii[E];
+    for (int c = tid; c < n_chunks; c += kFinishThreads) {
+      const int cnt = (int)(coff[c + 1] - coff[c]);
+      const uint2* src = a.cand + (bh * a.max_chunks + c) * (int64_t)cap_chunk;
+      const uint32_t dst = coff[c];
+      uint4 v[4];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int p = p0 + j;
-      if (j < per && p < (int)total) {
-        while (coff[c + 1] <= (uint32_t)p) ++c;
-        const int64_t src = (bh * a.max_chunks + c) * (int64_t)cap_chunk + (p - (int)coff[c]);
-        kk[j] = a.cand_key[src];
-        ii[j] = a.cand_idx[src];
+      for (int j = 0; j < 4; ++j) v[j] = reinterpret_cast<const uint4*>(src)[j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (2 * j < cnt) {
+          lkey[dst + 2 * j] = v[j].x;
+          lidx[dst + 2 * j] = (int32_t)v[j].y;
+        }
+        if (2 * j + 1 < cnt) {
+          lkey[dst + 2 * j + 1] = v[j].z;
+          lidx[dst + 2 * j + 1] = (int32_t)v[j].w;
+        }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int p = p0 + j;
-      if (j < per && p < (int)total) {
-        lkey[p] = kk[j];
-        lidx[p] = ii[j];
+      for (int i = 8; i < cnt; ++i) {
+        const uint2 e = src[i];
+        lkey[dst + i] = e.x;
+        lidx[dst + i] = (int32_t)e.y;
       }
     }
   }
@@ -506,7 +550,7 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
     return;
   }
   uint32_t kth, need;
-  radix_select_lds<kFinishThreads>(lkey, n, (uint32_t)K, hist, tmp, &kth, &need);
+  block_radix_select<kFinishThreads>(lkey, n, (uint32_t)K, hist, tmp, &kth, &need);
   // ordered compaction: thread owns a contiguous run of E' positions
   const int per = (n + kFinishThreads - 1) / kFinishThreads;
   const int i0 = tid * per, i1 = min(i0 + per, n);
