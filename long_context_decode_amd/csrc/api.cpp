@@ -82,8 +82,8 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   p->G = p->Hq / p->Hkv;
   p->dv = p->mla ? kMlaLatent : p->d;
   p->maxN = (int64_t)p->max_pages * p->P;
-  // stream chunking: one wavefront per chunk of 16 / (S / 16) pages
-  p->cp = std::max(1, 16 / (p->S / 16));
+  // stream chunking: one wavefront per chunk of 4 groups of 16 / (S / 16) pages
+  p->cp = 4 * std::max(1, 16 / (p->S / 16));
   p->max_chunks = (int)cdiv(p->max_pages, p->cp);
   if (p->max_chunks > kMaxChunks) return JSSA_ERR_UNSUPPORTED;
   split_plan(std::min<int64_t>(p->B, p->maxN), p->batch * p->Hkv, &p->sp_splits, &p->sp_len);

@@ -40,7 +40,7 @@ struct SelectArgs {
   const uint16_t* k_new;
   const int32_t* slot_new;
   int batch, Hq, Hkv, d, P, max_pages, r, S, B, G, mla;
-  int cp;               // pages per stream chunk (16 / (scoring dims / 16))
+  int cp;               // pages per stream chunk (4 groups of 16 / (scoring dims / 16))
   int max_chunks;
   int force_exact;
 };

@@ -9,13 +9,13 @@
 //     sample of the sequence's pages and picks a threshold key tau that about
 //     2B tokens should clear (tau = "all" when the whole sequence fits the
 //     candidate buffer).  In jssa_decode it also stores the new token.
-//  2. stream    (each wavefront owns one chunk of 16/R consecutive pages of
-//     one sequence for a group of KV heads): every lane owns one (KV head,
-//     slot) and reads that token's 16-byte FP8 pieces for all pages of the
-//     chunk at once (a wavefront reads one contiguous run per piece), scores
-//     them, and the keys >= tau are compacted in position order straight from
-//     the ballot masks into the chunk's own region of the candidate buffer;
-//     the chunk's count is recorded.
+//  2. stream    (each wavefront owns 16/R consecutive pages of one sequence
+//     for a group of KV heads; a block's four wavefronts form one chunk):
+//     every lane owns one (KV head, slot) and reads that token's 16-byte FP8
+//     pieces for all pages at once (a wavefront reads one contiguous run per
+//     piece), scores them, and the keys >= tau are compacted in position
+//     order straight from the ballot masks into the chunk's region of the
+//     candidate buffer; the chunk's count is recorded.
 //  3. finish    (one 1024-thread block per (sequence, KV head)): gathers the
 //     candidates into LDS in chunk order (so they are in position order),
 //     radix-selects the B-th largest key, and writes the winners ascending
@@ -345,23 +345,25 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 // ================================================================== 2. stream
 
 template <int R, int P>
-__global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
+__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(R <= 2 ? 4 : 1))) void select_stream(SelectArgs a) {
   constexpr int S = R * 16;
   constexpr int HPW = 64 / P;               // KV heads covered by one wavefront
-  constexpr int PF = R >= 16 ? 1 : 16 / R;  // pages of a chunk (all in flight at once)
+  constexpr int PF = R >= 16 ? 1 : 16 / R;  // pages of a wavefront (all in flight at once)
+  __shared__ uint32_t wcnt[4][HPW];
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
-  const int c = blockIdx.x * 4 + w, hg = blockIdx.y, b = blockIdx.z;
+  const int hg = blockIdx.x, c = blockIdx.y, b = blockIdx.z;   // chunk c = 4 wavefronts
   const int N = seq_len_of(a, b);
   const int n_pages = (N + P - 1) / P;
-  const int page0 = c * PF;
-  if (page0 >= n_pages) return;
+  if (c * a.cp >= n_pages) return;           // uniform over the block
+  const int page0 = c * a.cp + w * PF;
+  const bool any = page0 < n_pages;
   const int hl = lane / P, slot = lane % P;
   const int head = hg * HPW + hl;
   const bool active = head < a.Hkv;
   const int headc = active ? head : 0;
   const int64_t bh = (int64_t)b * a.Hkv + headc;
 
-  // physical pages of the chunk: lane i < PF holds page page0 + i
+  // physical pages of this wavefront: lane i < PF holds page page0 + i
   int phys_l = 0;
   if (lane < PF && page0 + lane < n_pages) phys_l = a.block_table[(int64_t)b * a.max_pages + page0 + lane];
   uint4 pc[PF][R];
@@ -388,36 +390,39 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
   const int64_t maxN = (int64_t)a.max_pages * P;
   float* sout = a.scores_out ? a.scores_out + bh * maxN : nullptr;
 
-  // keys, flags and the ballot mask of every page of the chunk
+  // keys and ballot masks of every page of the wavefront
   uint32_t key[PF];
   uint64_t mask[PF];
+  const uint64_t hmask = (P == 64) ? ~0ull : (((1ull << (P & 63)) - 1ull) << (hl * P));
+  uint32_t cnt = 0;
 #pragma unroll
   for (int f = 0; f < PF; ++f) {
     const int t = (page0 + f) * P + slot;
     key[f] = 0u;
-    if (active && t < N) {
+    if (any && active && t < N) {
       const float s = score_pieces<R>(pc[f], qh) * sc[f];
       key[f] = score_key(s);
       if (sout) sout[t] = s;
     }
-    mask[f] = ballot(key[f] >= tau);
+    mask[f] = ballot(key[f] >= tau) & hmask;
+    cnt += (uint32_t)__popcll(mask[f]);
   }
-  // per head: count of the chunk and its candidates, in position order, at the
-  // start of the chunk's own region of the candidate buffer (no atomics)
-  const uint64_t hmask = (P == 64) ? ~0ull : (((1ull << (P & 63)) - 1ull) << (hl * P));
-  uint32_t cnt = 0;
+  // the block's four wavefronts share one region: offsets from their counts
+  if (slot == 0) wcnt[w][hl] = cnt;
+  __syncthreads();
+  uint32_t run = 0, total = 0;
 #pragma unroll
-  for (int f = 0; f < PF; ++f) cnt += (uint32_t)__popcll(mask[f] & hmask);
-  const int64_t region = (bh * a.max_chunks + c) * (int64_t)(PF * P);
-  if (slot == 0 && active) a.chunk_cnt[bh * a.max_chunks + c] = (int32_t)cnt;
-  uint32_t run = 0;
+  for (int v = 0; v < 4; ++v) {
+    const uint32_t x = wcnt[v][hl];
+    run += v < w ? x : 0u;
+    total += x;
+  }
+  if (w == 0 && slot == 0 && active) a.chunk_cnt[bh * a.max_chunks + c] = (int32_t)total;
+  uint2* region = a.cand + (bh * a.max_chunks + c) * (int64_t)(a.cp * P);
 #pragma unroll
   for (int f = 0; f < PF; ++f) {
-    const uint64_t m = mask[f] & hmask;
-    if (m & (1ull << lane)) {
-      const int64_t pos = region + run + lanes_below(m);
-      a.cand[pos] = make_uint2(key[f], (uint32_t)((page0 + f) * P + slot));
-    }
+    const uint64_t m = mask[f];
+    if (m & (1ull << lane)) region[run + lanes_below(m)] = make_uint2(key[f], (uint32_t)((page0 + f) * P + slot));
     run += (uint32_t)__popcll(m);
   }
 }
@@ -514,19 +519,19 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   if (tid == 0) coff[n_chunks] = carry;
   __syncthreads();
   // gather the candidates in position order: thread c copies chunk c's
-  // contiguous run to its offset; the first 8 entries are read unconditionally
-  // (a region holds at least 32), the rest, if any, one by one
+  // contiguous run to its offset; the first 16 entries are read
+  // unconditionally (a region holds at least 128), the rest, if any, one by one
   {
     const int cap_chunk = a.cp * a.P;
     for (int c = tid; c < n_chunks; c += kFinishThreads) {
       const int cnt = (int)(coff[c + 1] - coff[c]);
       const uint2* src = a.cand + (bh * a.max_chunks + c) * (int64_t)cap_chunk;
       const uint32_t dst = coff[c];
-      uint4 v[4];
+      uint4 v[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = reinterpret_cast<const uint4*>(src)[j];
+      for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const uint4*>(src)[j];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 8; ++j) {
         if (2 * j < cnt) {
           lkey[dst + 2 * j] = v[j].x;
           lidx[dst + 2 * j] = (int32_t)v[j].y;
@@ -536,7 +541,7 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
           lidx[dst + 2 * j + 1] = (int32_t)v[j].w;
         }
       }
-      for (int i = 8; i < cnt; ++i) {
+      for (int i = 16; i < cnt; ++i) {
         const uint2 e = src[i];
         lkey[dst + i] = e.x;
         lidx[dst + i] = (int32_t)e.y;
@@ -589,8 +594,7 @@ hipError_t launch_select_rp(const SelectArgs& a, int stages, hipStream_t s) {
   }
   if (stages & 2) {
     const int hg = (a.Hkv + HPW - 1) / HPW;
-    hipLaunchKernelGGL((select_stream<R, P>), dim3((a.max_chunks + 3) / 4, hg, a.batch), dim3(kStreamThreads), 0,
-                       s, a);
+    hipLaunchKernelGGL((select_stream<R, P>), dim3(hg, a.max_chunks, a.batch), dim3(kStreamThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4) {
