@@ -79,7 +79,7 @@ enum { JSSA_SELECT_AUTO = 0, JSSA_SELECT_EXACT_STREAM = 1 };
 typedef struct jssa_shape {
   int32_t kind;               /* JSSA_KIND_GQA or JSSA_KIND_MLA */
   int32_t batch;              /* sequences in the step, >= 1 */
-  int32_t num_q_heads;        /* Hq; GQA: Hq % Hkv == 0, G = Hq/Hkv in {1,2,4,8}; MLA: multiple of 16, <= 128 */
+  int32_t num_q_heads;        /* Hq; GQA: Hq % Hkv == 0, G = Hq/Hkv in {1,2,4,8}; MLA: multiple of 32, <= 128 */
   int32_t num_kv_heads;       /* Hkv; MLA: 1 */
   int32_t head_dim;           /* d: GQA 128 or 256; MLA 576 */
   int32_t page_size;          /* tokens per page: 16, 32 or 64 */

@@ -23,6 +23,7 @@ struct Plan {
   int cp, max_chunks;
   int sp_splits, sp_len;     // sparse attention split plan
   int dn_splits, dn_len;     // dense (window 0) split plan
+  int ml_splits, ml_len;     // MLA sparse attention split plan
   size_t off_qhat, off_tau, off_chunk, off_cand, off_part_o, off_part_ml, total;
 };
 
@@ -59,7 +60,7 @@ int32_t validate_shape(const jssa_shape* sh) {
     if (sh->rank > std::min(sh->head_dim, 128)) return JSSA_ERR_UNSUPPORTED;
   } else {
     if (sh->num_kv_heads != 1 || sh->head_dim != kMlaLatent + kMlaRope) return JSSA_ERR_UNSUPPORTED;
-    if (sh->num_q_heads % 16 != 0 || sh->num_q_heads > 128) return JSSA_ERR_UNSUPPORTED;
+    if (sh->num_q_heads % 32 != 0 || sh->num_q_heads > 128) return JSSA_ERR_UNSUPPORTED;
     if (sh->rank > 64) return JSSA_ERR_UNSUPPORTED;
   }
   return JSSA_OK;
@@ -88,7 +89,15 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   if (p->max_chunks > kMaxChunks) return JSSA_ERR_UNSUPPORTED;
   split_plan(std::min<int64_t>(p->B, p->maxN), p->batch * p->Hkv, &p->sp_splits, &p->sp_len);
   split_plan(p->maxN, p->batch * p->Hkv, &p->dn_splits, &p->dn_len);
-  const int max_splits = std::max(p->sp_splits, p->dn_splits);
+  {
+    // MLA: blocks of (split, 32 heads, sequence), about 256 in all, 64-row tiles
+    const int64_t n = std::min<int64_t>(p->B, p->maxN);
+    int64_t sp = cdiv(256, (int64_t)p->batch * std::max(1, p->Hq / 32));
+    sp = std::max<int64_t>(1, std::min<int64_t>({sp, cdiv(n, 64), 64}));
+    p->ml_len = (int)(cdiv(cdiv(n, sp), 64) * 64);
+    p->ml_splits = (int)cdiv(n, p->ml_len);
+  }
+  const int max_splits = std::max({p->sp_splits, p->dn_splits, p->mla ? p->ml_splits : 1});
   const size_t bh = (size_t)p->batch * p->Hkv;
   const size_t cand = bh * p->max_chunks * p->cp * p->P;   // one region per stream chunk
   size_t off = 0;
@@ -172,8 +181,8 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
 int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, int window,
                   float sm_scale, uint16_t* out, float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (p.mla) return JSSA_ERR_UNSUPPORTED;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !ws) return JSSA_ERR_NULL;
+  if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !out || !ws) return JSSA_ERR_NULL;
+  if (p.mla && !indices) return JSSA_ERR_UNSUPPORTED;       // dense MLA baseline not built
   if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
   if (window < 0) return JSSA_ERR_SHAPE;
   AttendArgs a{};
@@ -196,6 +205,11 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
   a.B = p.B;
   a.G = p.G;
   a.window = indices ? 0 : window;
+  if (p.mla) {
+    a.splits = p.ml_splits;
+    a.split_len = p.ml_len;
+    return hip_status(launch_mla_attend(a, stream));
+  }
   if (indices) {
     a.splits = p.sp_splits;
     a.split_len = p.sp_len;
@@ -300,7 +314,6 @@ int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
   if (!p.mla && !v_cache) return JSSA_ERR_NULL;
   if (k_new && !slot_new) return JSSA_ERR_NULL;
   if (workspace_bytes < p.total) return JSSA_ERR_WORKSPACE;
-  if (p.mla) return JSSA_ERR_UNSUPPORTED;
   // the prologue of select stores the new token
   st = do_select(p, shape->select_mode, JSSA_STAGE_ALL, q, M, kp, kp_scale, block_table, seq_lens, indices, nullptr,
                  workspace, workspace_bytes, stream, k_new, k_new ? slot_new : nullptr);

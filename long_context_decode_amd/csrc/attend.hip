@@ -303,8 +303,7 @@ hipError_t launch_dg(const AttendArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((attend_kernel<D, G, true>), dim3(a.splits, a.Hkv, a.batch), dim3(kAttendThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel<D>, dim3(a.Hq, a.batch), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_merge(a, D, s);
 }
 
 template <int D>
@@ -319,6 +318,16 @@ hipError_t launch_d(const AttendArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_merge(const AttendArgs& a, int dv, hipStream_t s) {
+  switch (dv) {
+    case 128: hipLaunchKernelGGL(merge_kernel<128>, dim3(a.Hq, a.batch), dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(merge_kernel<256>, dim3(a.Hq, a.batch), dim3(256), 0, s, a); break;
+    case 512: hipLaunchKernelGGL(merge_kernel<512>, dim3(a.Hq, a.batch), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_attend(const AttendArgs& a, int head_dim, hipStream_t s) {
   switch (head_dim) {

@@ -74,6 +74,8 @@ struct CalibArgs {
 hipError_t launch_store(const StoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int stages, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_mla_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_merge(const AttendArgs& a, int dv, hipStream_t s);
 hipError_t launch_calib(const CalibArgs& a, hipStream_t s);
 
 // host: per-head top-r eigenvectors of the unit-trace-normalised moment sum

@@ -1,0 +1,218 @@
+// MLA sparse attention over the selected latent rows (README page, paper-to-code
+// map: JSSA on MLA uses FlashMLA sparse attention over the selected positions;
+// summary page §3.4: 64 latent + 64 RoPE scoring dims).  Every query head of
+// sequence b attends to the same B selected rows [c (512) ; k_pe (64)]: logits
+// sm * q . row over all 576 dims, values = the first 512 dims of the row.
+//
+// This is a dense contraction per sequence (Q 128x576 times 576xB, then
+// P 128xB times Bx512), so it runs on the matrix cores: v_mfma_f32_16x16x32_bf16
+// (lane l holds A[l%16][8(l/16)..+8], B[8(l/16)..+8][l%16] and returns
+// D[4(l/16)+j][l%16]).
+//
+// Block = (split of the selected rows, block of 32 query heads, sequence),
+// 4 wavefronts.  Per tile of 64 rows:
+//   * the rows are gathered once into LDS (row stride 584 elements);
+//   * S = Q K^T: wavefront w computes the 32 heads x 16 rows [16w, 16w+16)
+//     over 18 K-steps, Q coming from LDS;
+//   * online softmax per head (base 2): tile max and sum are combined across
+//     the four wavefronts through LDS, the running state rescales the output;
+//   * O += P V: wavefront w owns output dims [128w, 128w+128) (2 x 8 tiles of
+//     16x16); P comes from LDS, V is read column-wise from the same LDS tile.
+//     Within each group of 32 rows the K index g*8+i of lane group g maps to
+//     row 4i+g, so the four lane groups read rows on different LDS banks; P is
+//     stored in that order.
+// The split's partial (unnormalised o, running max, running sum) goes to the
+// workspace and merge_kernel<512> combines the splits.
+#include "common.h"
+#include "kernels.h"
+
+namespace jssa {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = kMlaLatent + kMlaRope;  // 576
+constexpr int kV = kMlaLatent;             // 512
+constexpr int kHB = 32;                    // query heads per block
+constexpr int kTile = 64;                  // selected rows per tile
+constexpr int kRow = kD + 8;               // LDS row stride of K rows and Q rows (elements)
+constexpr int kPRow = kTile + 8;           // LDS row stride of P (elements)
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0x128>(x));
+  x = fmaxf(x, dpp_f<0x124>(x));
+  x = fmaxf(x, dpp_f<0x122>(x));
+  x = fmaxf(x, dpp_f<0x121>(x));
+  return x;
+}
+
+// K index (0..63) of row t of a tile in the P / V operand order.
+__device__ __forceinline__ int k_of_row(int t) { return (t & 32) + (t & 3) * 8 + ((t & 31) >> 2); }
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
+  __shared__ __align__(16) uint16_t Kt[kTile * kRow];
+  __shared__ __align__(16) uint16_t Qs[kHB * kRow];
+  __shared__ __align__(16) uint16_t Ps[kHB * kPRow];
+  __shared__ float red_m[4][kHB];
+  __shared__ float red_l[4][kHB];
+  __shared__ int rows[kTile];
+
+  const int s = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  const int tid = (int)threadIdx.x, l = lane_id(), w = tid >> 6;
+  const int g = l >> 4, c = l & 15;
+  int N = a.seq_lens[b];
+  const int cap = a.max_pages * a.P;
+  N = N < 0 ? 0 : (N > cap ? cap : N);
+  const int n_tok = N < a.B ? N : a.B;
+  const int i0 = s * a.split_len;
+  if (i0 >= n_tok) return;
+  const int i1 = min(i0 + a.split_len, n_tok);
+  const int32_t* idx = a.indices + (int64_t)b * a.B;    // Hkv = 1
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+
+  // Q of the 32 heads into LDS
+  for (int u = tid; u < kHB * (kD / 8); u += kThreads) {
+    const int m = u / (kD / 8), cc = u % (kD / 8);
+    *reinterpret_cast<uint4*>(&Qs[m * kRow + cc * 8]) =
+        *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + hb * kHB + m) * kD + cc * 8);
+  }
+
+  // lane state: heads mt*16 + 4g + j (mt = 0, 1; j = 0..3)
+  float m_run[2][4], l_run[2][4];
+  f32x4 O[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m_run[mt][j] = -INFINITY;
+      l_run[mt][j] = 0.0f;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) O[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  for (int t0 = i0; t0 < i1; t0 += kTile) {
+    __syncthreads();                                   // previous tile fully consumed
+    if (tid < kTile) {
+      const int ii = t0 + tid;
+      int r = -1;
+      if (ii < i1) {
+        const int t = idx[ii];
+        if (t >= 0) r = bt[t / a.P] * a.P + (t % a.P);
+      }
+      rows[tid] = r;
+    }
+    __syncthreads();
+    for (int u = tid; u < kTile * (kD / 8); u += kThreads) {
+      const int tt = u / (kD / 8), cc = u % (kD / 8);
+      const int r = rows[tt];
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r >= 0) v = *reinterpret_cast<const uint4*>(a.k_cache + (int64_t)r * kD + cc * 8);
+      *reinterpret_cast<uint4*>(&Kt[tt * kRow + cc * 8]) = v;
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T for rows [16w, 16w + 16)
+    f32x4 S[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll 6
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&Kt[(w * 16 + c) * kRow + ks * 32 + g * 8]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qs[(mt * 16 + c) * kRow + ks * 32 + g * 8]);
+        S[mt] = mfma16(aq, bk, S[mt]);
+      }
+    }
+    const bool valid = rows[w * 16 + c] >= 0;
+    float x[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[mt][j] = valid ? S[mt][j] * a.sm_log2 : -INFINITY;
+        const float tm = row16_max(x[mt][j]);
+        if (c == 0) red_m[w][mt * 16 + g * 4 + j] = tm;
+      }
+    __syncthreads();
+    // ---- softmax update (every wavefront computes the same state)
+    const int kpos = k_of_row(w * 16 + c);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int hh = mt * 16 + g * 4 + j;
+        const float tm = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
+        const float mn = fmaxf(m_run[mt][j], tm);
+        const float ms = (mn == -INFINITY) ? 0.0f : mn;
+        const float al = __builtin_amdgcn_exp2f(m_run[mt][j] - ms);
+        const float p = __builtin_amdgcn_exp2f(x[mt][j] - ms);
+        const float ps = row16_sum(p);
+        if (c == 0) red_l[w][hh] = ps;
+        l_run[mt][j] *= al;
+        m_run[mt][j] = mn;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) O[mt][nt][j] *= al;
+        Ps[hh * kPRow + kpos] = __builtin_bit_cast(uint16_t, (__bf16)p);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int hh = mt * 16 + g * 4 + j;
+        l_run[mt][j] += (red_l[0][hh] + red_l[1][hh]) + (red_l[2][hh] + red_l[3][hh]);
+      }
+
+    // ---- O += P V for output dims [128w, 128w + 128)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 ap[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        ap[mt] = *reinterpret_cast<const bf16x8*>(&Ps[(mt * 16 + c) * kPRow + kk * 32 + g * 8]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int dim = w * 128 + nt * 16 + c;
+        uint16_t vv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vv[i] = Kt[(kk * 32 + 4 * i + g) * kRow + dim];
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vv));
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) O[mt][nt] = mfma16(ap[mt], bv, O[mt][nt]);
+      }
+    }
+  }
+
+  // ---- this split's partial
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int head = hb * kHB + mt * 16 + g * 4 + j;
+      const int64_t pj = ((int64_t)b * a.Hq + head) * a.splits + s;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) a.part_o[pj * kV + w * 128 + nt * 16 + c] = O[mt][nt][j];
+      if (w == 0 && c == 0) {
+        a.part_ml[pj * 2] = m_run[mt][j];
+        a.part_ml[pj * 2 + 1] = l_run[mt][j];
+      }
+    }
+}
+
+hipError_t launch_mla_attend(const AttendArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(mla_attend_kernel, dim3(a.splits, a.Hq / kHB, a.batch), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge(a, kV, s);
+}
+
+}  // namespace jssa

@@ -448,3 +448,65 @@ def test_budget_one_and_all_equal_scores():
                       torch.from_numpy(bt).to(DEV), torch.tensor([w.seq_len], dtype=torch.int32, device=DEV), idx,
                       L.alloc_workspace(shape))
         assert np.all(idx.cpu().numpy() == 0)
+
+
+# ----------------------------------------------------------------------------- MLA attention (MFMA)
+
+@pytest.mark.parametrize("name", list(MLA_CASES))
+def test_mla_attend_parity(name):
+    w, case, m32, rows, stored = _mla(name)
+    q = bf16_bits(case.q)
+    idx = np.full((w.batch, 1, w.budget), -1, np.int32)
+    for b in range(w.batch):
+        qhat = omla.project_query(q[b], m32)
+        s = ogqa.scores(qhat, stored[b][0], stored[b][1])
+        idx[b, 0], _ = ogqa.select_topb(s, w.budget)
+    shape = L.shape_for(w)
+    out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    L.jssa_attend(shape, case.q.to(DEV), case.latent.to(DEV), None, case.block_table.to(DEV), case.seq_lens.to(DEV),
+                  torch.from_numpy(idx).to(DEV), w.sm_scale, out, L.alloc_workspace(shape), lse)
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(w.batch):
+        sel = idx[b, 0][idx[b, 0] >= 0]
+        o, l = omla.attend(q[b], rows[b][sel], w.sm_scale)
+        err = check_attention(got[b], o)
+        assert np.all(np.abs(glse[b] - l) <= 1e-3), np.abs(glse[b] - l).max()
+        print(f"{name} b{b}: max abs {err[0]:.2e} mean abs {err[1]:.2e}")
+
+
+def test_mla_decode_step():
+    w, case, m32, rows, stored = _mla("mla_sampled")
+    shape = L.shape_for(w)
+    bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
+    prev = [(c.copy(), s.copy()) for c, s in stored]
+    for b in range(w.batch):
+        prev[b][0][-1] = 0
+        prev[b][1][-1] = 0
+    kp, ks = pack_kp([c[:, None, :] for c, _ in prev], [s[:, None] for _, s in prev], bt, w.page_size,
+                     case.latent.shape[0], sl)
+    kp, ks = torch.from_numpy(kp).to(DEV), torch.from_numpy(ks).to(DEV)
+    new_slot = np.array([bt[b, (sl[b] - 1) // w.page_size] * w.page_size + (sl[b] - 1) % w.page_size
+                         for b in range(w.batch)], np.int32)
+    k_new = torch.from_numpy(np.stack([rows[b][-1] for b in range(w.batch)]).view(np.int16)).view(torch.bfloat16)
+    idx = torch.empty((w.batch, 1, w.budget), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+    L.jssa_decode(shape, case.q.to(DEV), k_new.to(DEV), torch.from_numpy(new_slot).to(DEV),
+                  torch.from_numpy(m32).to(DEV), kp, ks, case.latent.to(DEV), None, case.block_table.to(DEV),
+                  case.seq_lens.to(DEV), idx, w.sm_scale, out, L.alloc_workspace(shape))
+    kp_h, ks_h = kp.cpu().numpy(), ks.cpu().numpy()
+    gidx, got = idx.cpu().numpy(), out.float().cpu().numpy()
+    q = bf16_bits(case.q)
+    for b in range(w.batch):
+        n = int(sl[b])
+        c, s = unpack_kp(kp_h, ks_h, bt[b], n, w.page_size)
+        check_codes(c[-1:, 0], stored[b][0][-1:], max_frac=1.0 / 64)
+        codes_b, scale_b = stored[b][0].copy(), stored[b][1].copy()
+        codes_b[-1], scale_b[-1] = c[-1, 0], s[-1, 0]
+        qhat = omla.project_query(q[b], m32)
+        sc = ogqa.scores(qhat, codes_b, scale_b)
+        oidx, tau = ogqa.select_topb(sc, w.budget)
+        check_selection(gidx[b, 0], oidx, sc, tau)
+        sel = gidx[b, 0][gidx[b, 0] >= 0]
+        o, _ = omla.attend(q[b], rows[b][sel], w.sm_scale)
+        check_attention(got[b], o)
