@@ -1,23 +1,36 @@
 #!/usr/bin/env python
-"""Benchmark of one JSSA decode step on one MI355X.
+"""Benchmark of the JSSA decode attention stage on one MI355X.
 
-A step is one jssa_decode call over the whole batch of one layer: store the
-new token's projected key, select (qhat + sampled threshold, FP8 score stream
-over every cached token, exact top-B) and gather-free attention with the
-split-K merge.  The workload (default: the Llama-3.1-8B-shaped layer at 128K,
-batch 8) is synthetic and seeded; its basis M comes from the library's own
-calibration (jssa_calib_moments + jssa_basis) on synthetic calibration
-sequences.  Inputs are resident in HBM before the timed region; three cache
-replicas are rotated so the 256 MB Infinity Cache cannot serve a step from
-the previous one.  Also timed: the dense full-KV decode on the same caches
-(speedup), each stage alone with HIP events (roofline of the dominant
-kernel), and the CPU oracle on a bounded sample (cpu_baseline).
+A step is one decode step of the whole batch through the library's C ABI:
+for a single-layer workload one jssa_decode call (store the new token's
+projected key, select = qhat + sampled threshold, FP8 score stream over every
+cached token, exact top-B, then gather-free attention with the split-K
+merge); for the hybrid stack all of its layers in order (sliding-window layers
+through jssa_full_decode, global layers through jssa_decode, each with its own
+basis).  The default workload is the Llama-3.1-8B-shaped layer at 128K,
+batch 8.  Inputs are synthetic and seeded; each basis M comes from the
+library's own calibration (jssa_calib_moments + jssa_basis) on synthetic
+calibration sequences.  Everything is resident in HBM before the timed region;
+cache replicas are rotated when one step's bytes would fit in the 256 MB
+Infinity Cache.
 
+Also measured: the same steps captured in HIP graphs, the dense full-KV decode
+on the same caches (speedup), each stage alone with HIP events (roofline of
+the dominant kernel) and the CPU oracle on a bounded sample (cpu_baseline).
 Prints one JSON line.
+
+Two helper modes turn rocprofv3 output into the short summaries kept under
+profiles/:
+  --summarize-trace DIR   kernel-trace statistics -> markdown table
+  --summarize-counters FETCH_DIR WRITE_DIR   FETCH_SIZE / WRITE_SIZE per
+      dispatch of the score-stream kernel, scaled by the same counters on the
+      1 GiB elementwise probe (--copy-probe) -> JSON read back by this script
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -28,7 +41,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "counters_select_stream_llama8b_128k.json")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+STREAM_KERNEL = "select_stream"
+PROBE_KERNEL = "neg_kernel"           # torch's elementwise negation kernel: the 1 GiB probe
+PROBE_BYTES = 1 << 30                 # fp32 neg over 2^28 elements: 1 GiB read, 1 GiB written
+STREAM_SOURCES = ("select.hip", "common.h", "kernels.h")
+METRIC = "decode attn-stage steps/s @128K; HBM GB/s vs peak; speedup vs full-KV decode"
+
+
+def counters_path(workload):
+    return os.path.join(ROOT, "profiles", f"counters_select_stream_{workload}.json")
 
 
 def _src_hash(*names):
@@ -39,156 +61,391 @@ def _src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, seq_lens, sparse=True):
-    """Bytes the method itself must move per step (roofline)."""
-    S = w.score_dims
-    d, hkv, hq, B = w.head_dim, w.num_kv_heads, w.num_q_heads, w.budget
-    io = 2 * w.batch * hq * d * 2 + w.batch * w.pages_per_seq * 4
-    if not sparse:
-        return sum(n * hkv * 2 * d * 2 for n in seq_lens) + io, {}
-    score = sum(n * hkv * (S + 4) for n in seq_lens)
-    kv = sum(min(B, n) * hkv * 2 * d * 2 for n in seq_lens)
-    idx = w.batch * hkv * B * 4 * 2
-    store = w.batch * hkv * (d * 2 + S + 4)
-    parts = dict(score=score, selected_kv=kv, indices=idx, q_out_table=io, store=store)
+# ----------------------------------------------------------------------------- algorithmic bytes
+
+def layer_bytes(w, seq_lens, mode):
+    """Bytes one layer must move per step.  mode: 'sparse' (JSSA), 'full' (all positions), 'window'."""
+    S, d, hkv, hq, B = w.score_dims, w.head_dim, w.num_kv_heads, w.num_q_heads, w.budget
+    row = d * 2 if w.kind == "mla" else 2 * d * 2    # one latent row (K = V) / one K + V pair per KV head
+    io = w.batch * hq * (d + w.v_dim) * 2 + w.batch * w.pages_per_seq * 4
+    if mode == "full":
+        return {"kv": sum(n * hkv * row for n in seq_lens), "q_out_table": io}
+    if mode == "window":      # only the window's pages of the block table are read
+        io_w = w.batch * hq * (d + w.v_dim) * 2 + w.batch * (-(-w.window // w.page_size)) * 4
+        return {"kv": sum(min(n, w.window) * hkv * row for n in seq_lens), "q_out_table": io_w}
+    return {"score": sum(n * hkv * (S + 4) for n in seq_lens),
+            "selected_kv": sum(min(B, n) * hkv * row for n in seq_lens),
+            "indices": w.batch * hkv * B * 4 * 2,
+            "q_out_table": io,
+            "store": w.batch * hkv * (d * 2 + S + 4)}
+
+
+def step_bytes(w, seq_lens, sparse=True):
+    """Sum over the step's layers, with the per-part breakdown."""
+    parts = {}
+    for l in range(w.num_layers if w.window else 1):
+        if w.window and l in w.window_layers():
+            p = {"window_" + k: v for k, v in layer_bytes(w, seq_lens, "window").items()}
+        else:
+            p = layer_bytes(w, seq_lens, "sparse" if sparse else "full")
+        for k, v in p.items():
+            parts[k] = parts.get(k, 0) + v
     return sum(parts.values()), parts
 
 
-def setup(w, device, replicas):
-    import numpy as np
+def mla_attend_flops(w, seq_lens, sparse=True):
+    """2 * Hq * (576 + 512) flops per attended row and sequence."""
+    n = sum(min(w.budget, s) if sparse else s for s in seq_lens)
+    return 2 * w.num_q_heads * (w.head_dim + w.v_dim) * n
+
+
+# ----------------------------------------------------------------------------- setup
+
+def calibrate_gqa(L, w, layer, device):
     import torch
-
-    import long_context_decode_amd as L
-    from synth import make_gqa_calibration, make_gqa_case
-
+    from synth import make_gqa_calibration
     shape = L.shape_for(w)
-    # calibration with the library: moments on the GPU, eigenvectors on the host
-    qc, kc = make_gqa_calibration(w, 0, device=device)
+    qc, kc = make_gqa_calibration(w, layer, device=device)
     T = qc.shape[0]
     gq = torch.zeros((w.num_kv_heads, w.head_dim, w.head_dim), dtype=torch.float32, device=device)
     gk = torch.zeros_like(gq)
-    cws = torch.empty(L.calib_workspace_bytes(shape, T), dtype=torch.uint8, device=device)
-    L.jssa_calib_moments(shape, qc, kc, gq, gk, cws)
-    M = torch.from_numpy(L.jssa_basis(shape, gq.cpu().numpy(), gk.cpu().numpy())).to(device)
-    del qc, kc, cws
-    case = make_gqa_case(w, device=device, layers=[0])
-    lay = case.layers[0]
-    n_pages = lay.k_cache.shape[0]
-    kp, ks = L.alloc_scoring_cache(shape, n_pages, device)
-    # bulk store of every cached position
+    ws = torch.empty(L.calib_workspace_bytes(shape, T), dtype=torch.uint8, device=device)
+    L.jssa_calib_moments(shape, qc, kc, gq, gk, ws)
+    return torch.from_numpy(L.jssa_basis(shape, gq.cpu().numpy(), gk.cpu().numpy())).to(device)
+
+
+def calibrate_mla(L, w, device):
+    import torch
+    from synth import make_mla_calibration
+    shape = L.shape_for(w)
+    gq = torch.zeros((1, w.latent_dim, w.latent_dim), dtype=torch.float32, device=device)
+    gk = torch.zeros_like(gq)
+    ws = torch.empty(L.calib_workspace_bytes(shape, 2048), dtype=torch.uint8, device=device)
+    for qc, lat in make_mla_calibration(w, device=device, chunk=2048):
+        L.jssa_calib_moments(shape, qc, lat, gq, gk, ws)
+    return torch.from_numpy(L.jssa_basis(shape, gq.cpu().numpy(), gk.cpu().numpy())[0]).to(device)
+
+
+def bulk_store(L, w, shape, keys_flat, block_table, seq_lens, M, kp, ks):
+    """Store every cached position (rows gathered in logical order, 128K tokens per call)."""
+    import torch
     P = w.page_size
-    bt = case.block_table.long()
-    flat_k = lay.k_cache.view(-1, w.num_kv_heads, w.head_dim)
+    bt = block_table.long()
     for b in range(w.batch):
-        n = int(case.seq_lens[b])
+        n = int(seq_lens[b])
         for t0 in range(0, n, 1 << 17):
-            t = torch.arange(t0, min(n, t0 + (1 << 17)), device=device)
+            t = torch.arange(t0, min(n, t0 + (1 << 17)), device=keys_flat.device)
             slots = (bt[b, t // P] * P + t % P).to(torch.int32)
-            L.jssa_store(shape, flat_k[slots.long()].contiguous(), slots, M, kp, ks, check_slots=False)
-    last = case.seq_lens.long() - 1
-    slot_new = (bt[torch.arange(w.batch, device=device), last // P] * P + last % P).to(torch.int32)
-    k_new = flat_k[slot_new.long()].contiguous()
-    reps = [(kp, ks, lay.k_cache, lay.v_cache)]
+            L.jssa_store(shape, keys_flat[slots.long()].contiguous(), slots, M, kp, ks, check_slots=False)
+
+
+def new_token(w, keys_flat, block_table, seq_lens):
+    """Key and slot of position N-1 of every sequence (the token being decoded)."""
+    import torch
+    P = w.page_size
+    bt = block_table.long()
+    last = seq_lens.long() - 1
+    slot = (bt[torch.arange(w.batch, device=bt.device), last // P] * P + last % P).to(torch.int32)
+    return keys_flat[slot.long()].contiguous(), slot
+
+
+class Layer:
+    """Device state of one layer: inputs, caches and (global layers) basis + scoring cache."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def setup(w, device, replicas):
+    """Returns (shape, layers of every replica, block_table, seq_lens, generated case)."""
+    import torch
+    import long_context_decode_amd as L
+    from synth import make_gqa_case, make_mla_case
+
+    shape = L.shape_for(w)
+    if w.kind == "mla":
+        M = calibrate_mla(L, w, device)
+        case = make_mla_case(w, device=device)
+        kp, ks = L.alloc_scoring_cache(shape, case.latent.shape[0], device)
+        flat = case.latent.view(-1, w.head_dim)
+        bulk_store(L, w, shape, flat, case.block_table, case.seq_lens, M, kp, ks)
+        k_new, slot_new = new_token(w, flat, case.block_table, case.seq_lens)
+        base = [Layer(window=0, q=case.q, kc=case.latent, vc=None, M=M, kp=kp, ks=ks, k_new=k_new,
+                      slot_new=slot_new)]
+    else:
+        case = make_gqa_case(w, device=device, layers=list(range(w.num_layers if w.window else 1)))
+        base = []
+        for l, lay in sorted(case.layers.items()):
+            if w.window and l in w.window_layers():
+                base.append(Layer(window=w.window, q=lay.q, kc=lay.k_cache, vc=lay.v_cache))
+                continue
+            M = calibrate_gqa(L, w, l, device)
+            kp, ks = L.alloc_scoring_cache(shape, lay.k_cache.shape[0], device)
+            flat = lay.k_cache.view(-1, w.num_kv_heads, w.head_dim)
+            bulk_store(L, w, shape, flat, case.block_table, case.seq_lens, M, kp, ks)
+            k_new, slot_new = new_token(w, flat, case.block_table, case.seq_lens)
+            base.append(Layer(window=0, q=lay.q, kc=lay.k_cache, vc=lay.v_cache, M=M, kp=kp, ks=ks,
+                              k_new=k_new, slot_new=slot_new))
+    reps = [base]
     for _ in range(replicas - 1):
-        reps.append(tuple(x.clone() for x in reps[0]))
+        reps.append([Layer(**{k: (v.clone() if k in ("kc", "vc", "kp", "ks") and v is not None else v)
+                              for k, v in lay.__dict__.items()}) for lay in base])
     torch.cuda.synchronize()
-    return shape, M, case, reps, k_new, slot_new, case.block_table.to(device), case.seq_lens.to(device)
+    return shape, reps, case.block_table.to(device), case.seq_lens.to(device), case
 
 
-def time_steps(fn, steps, warmup, n_rep):
+# ----------------------------------------------------------------------------- timing
+
+def _quantiles(xs):
+    s = sorted(xs)
+
+    def q(p):
+        return s[min(len(s) - 1, max(0, int(round(p * (len(s) - 1)))))]
+    return q(0.5), q(0.1), q(0.9)
+
+
+def time_steps(fn, steps, warmup, n_rep, blocks=5):
+    """K steps in one timed region (events at block boundaries, no sync inside), bracketed by
+    synchronisations.  Returns (mean ms/step, block median, p10, p90, host wall ms/step)."""
     import torch
     for i in range(warmup):
         fn(i % n_rep)
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    blocks = max(1, min(blocks, steps))
+    bounds = [round(i * steps / blocks) for i in range(blocks + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in bounds]
     t0 = time.perf_counter()
-    start.record()
-    for i in range(steps):
-        fn(i % n_rep)
-    stop.record()
+    ev[0].record()
+    for k in range(blocks):
+        for i in range(bounds[k], bounds[k + 1]):
+            fn(i % n_rep)
+        ev[k + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(stop) / steps, wall * 1e3 / steps
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per_block = [ev[k].elapsed_time(ev[k + 1]) / (bounds[k + 1] - bounds[k]) for k in range(blocks)]
+    med, p10, p90 = _quantiles(per_block)
+    return ev[0].elapsed_time(ev[-1]) / steps, med, p10, p90, wall
+
+
+def time_graph(fn, steps, warmup, n_rep):
+    """The same step captured once per replica in a HIP graph; the graphs replayed back to back."""
+    import torch
+    graphs = []
+    for r in range(n_rep):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(r)
+        graphs.append(g)
+    total, med, p10, p90, _ = time_steps(lambda r: graphs[r].replay(), steps, warmup, n_rep)
+    return total, med, p10, p90
 
 
 def time_stages(stage_fns, steps, n_rep):
-    """Average duration of each stage, each bracketed by its own HIP events on the current stream."""
+    """Average duration of each stage: `steps` back-to-back launches of that stage alone (rotating the
+    replicas) between two HIP events on the current stream, the stream every library call launches on.
+    A kernel that runs longer than the host needs to issue the next call is timed exactly (the launches
+    queue up with no idle gap); shorter ones read high by the host's launch interval."""
     import torch
-    names = list(stage_fns)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
-          for _ in range(steps)]
-    for i in range(steps):
-        for j, n in enumerate(names):
-            ev[i][j][0].record()
-            stage_fns[n](i % n_rep)
-            ev[i][j][1].record()
-    torch.cuda.synchronize()
-    return {n: sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)) / steps
-            for j, n in enumerate(names)}
+    res = {}
+    for name, fn in stage_fns.items():
+        for i in range(2):
+            fn(i % n_rep)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            fn(i % n_rep)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    return res
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+
+def _host_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
 
 
 def cpu_baseline(w, case, n_seqs):
-    """The oracle (as is) on host cores: select + attend for n_seqs sequences, all KV heads, scaled to a step."""
+    """The oracle (as is) on host cores: store (untimed), then select + attend of n_seqs sequences of the
+    first layer, every KV head, scaled to one step."""
     import numpy as np
     import torch
     from oracle import calibrate as ocal
     from oracle import gqa as ogqa
-    from synth import bf16_bits, make_gqa_calibration
+    from oracle import mla as omla
+    from synth import bf16_bits, make_gqa_calibration, make_mla_calibration
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    qc, kc = make_gqa_calibration(w, 0, device="cpu")
-    m32 = ocal.calibrate(ocal.bf16_to_f64(bf16_bits(qc)), ocal.bf16_to_f64(bf16_bits(kc)), w.group,
-                         w.rank).astype(np.float32)
-    lay = case.layers[0]
-    bt = case.block_table.cpu().numpy()
-    q = bf16_bits(lay.q)
     elapsed = 0.0
-    for b in range(n_seqs):
-        n = int(case.seq_lens[b])
-        t = torch.arange(n, device=lay.k_cache.device)
-        pg = case.block_table[b].long()[t // w.page_size]
-        kr = bf16_bits(lay.k_cache[pg, t % w.page_size])
-        vr = bf16_bits(lay.v_cache[pg, t % w.page_size])
-        codes, scale = ogqa.store(kr, m32)                       # cache construction: not timed
-        t0 = time.perf_counter()
-        ogqa.decode_step(q[b], kr, vr, m32, w.budget, w.sm_scale, codes=codes, scale=scale)
-        elapsed += time.perf_counter() - t0
+    bt = case.block_table
+    if w.kind == "mla":
+        chunks = ((ocal.bf16_to_f64(bf16_bits(q)), ocal.bf16_to_f64(bf16_bits(l)))
+                  for q, l in make_mla_calibration(w, chunk=512))
+        m32 = omla.calibrate(chunks, w.latent_dim, w.rank)[0].astype(np.float32)
+        q = bf16_bits(case.q)
+        for b in range(n_seqs):
+            n = int(case.seq_lens[b])
+            t = torch.arange(n, device=case.latent.device)
+            rows = bf16_bits(case.latent[bt[b].long()[t // w.page_size], t % w.page_size])
+            codes, scale = omla.store(rows, m32)
+            t0 = time.perf_counter()
+            omla.decode_step(q[b], rows, m32, w.budget, w.sm_scale, codes=codes, scale=scale)
+            elapsed += time.perf_counter() - t0
+    else:
+        qc, kc = make_gqa_calibration(w, 0, device="cpu")
+        m32 = ocal.calibrate(ocal.bf16_to_f64(bf16_bits(qc)), ocal.bf16_to_f64(bf16_bits(kc)), w.group,
+                             w.rank).astype(np.float32)
+        lay = case.layers[0]
+        q = bf16_bits(lay.q)
+        for b in range(n_seqs):
+            n = int(case.seq_lens[b])
+            t = torch.arange(n, device=lay.k_cache.device)
+            pg = bt[b].long()[t // w.page_size]
+            kr = bf16_bits(lay.k_cache[pg, t % w.page_size])
+            vr = bf16_bits(lay.v_cache[pg, t % w.page_size])
+            codes, scale = ogqa.store(kr, m32)
+            t0 = time.perf_counter()
+            ogqa.decode_step(q[b], kr, vr, m32, w.budget, w.sm_scale, codes=codes, scale=scale)
+            elapsed += time.perf_counter() - t0
     per_step = elapsed * w.batch / n_seqs
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_seqs} of {w.batch} sequences x {w.num_kv_heads} KV heads (score + top-B + attend, "
-                      f"fp64 NumPy), {elapsed:.1f} s, scaled x{w.batch / n_seqs:g} to one step"}
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except Exception:  # pragma: no cover
+        pass
+    return {"value": round(1.0 / per_step, 4), "unit": "steps/s", "cores": int(_host_threads()), "kind": "oracle",
+            "sample": f"{n_seqs} of {w.batch} sequences of one layer (store untimed; select + attend, fp64 NumPy, "
+                      f"every KV head), {elapsed:.1f} s, scaled x{w.batch / n_seqs:g} to one step; host {cpu}"}
 
 
-def traffic_for(launch_bytes):
-    """HBM bytes per dispatch from committed rocprofv3 counters, if they were taken on the current kernel."""
-    if not os.path.exists(COUNTERS):
+# ----------------------------------------------------------------------------- counters
+
+def traffic_for(workload):
+    """HBM bytes per dispatch of the score-stream kernel from committed rocprofv3 counters, if they were
+    taken on the current kernel source."""
+    path = counters_path(workload)
+    if not os.path.exists(path):
         return None
-    c = json.load(open(COUNTERS))
-    if c.get("source_hash") != _src_hash("select.hip", "common.h"):
+    c = json.load(open(path))
+    if c.get("source_hash") != _src_hash(*STREAM_SOURCES):
         return None
     return c.get("hbm_bytes_per_dispatch")
 
+
+def _rows(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    out = []
+    for f in files:
+        with open(f, newline="") as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def _counter_per_dispatch(d, counter, match):
+    """Mean over the dispatches of kernels whose name contains `match` of one counter (summed over its
+    instances within a dispatch)."""
+    per = {}
+    for r in _rows(d, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter or match not in r.get("Kernel_Name", ""):
+            continue
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r.get("Kernel_Name"))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{counter}: no dispatch of a kernel matching {match!r} in {d}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_counters(fetch_dir, write_dir, workload, score_bytes, command):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the stream kernel, each scaled by the ratio of the probe's
+    known bytes to what the same counter reads for it."""
+    f_st, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", STREAM_KERNEL)
+    w_st, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", STREAM_KERNEL)
+    f_pr, _ = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", PROBE_KERNEL)
+    w_pr, _ = _counter_per_dispatch(write_dir, "WRITE_SIZE", PROBE_KERNEL)
+    kf = PROBE_BYTES / (f_pr * 1024.0)
+    kw = PROBE_BYTES / (w_pr * 1024.0)
+    hbm = f_st * 1024.0 * kf + w_st * 1024.0 * kw
+    return {"kernel": "select_stream", "workload": workload, "source_hash": _src_hash(*STREAM_SOURCES),
+            "fetch_kib_per_dispatch": round(f_st, 1), "write_kib_per_dispatch": round(w_st, 1),
+            "dispatches": [nf, nw], "probe_fetch_kib": round(f_pr, 1), "probe_write_kib": round(w_pr, 1),
+            "scale_fetch": round(kf, 4), "scale_write": round(kw, 4),
+            "hbm_bytes_per_dispatch": int(hbm), "algorithmic_bytes_per_dispatch": int(score_bytes),
+            "traffic_over_algorithmic": round(hbm / score_bytes, 4), "command": command}
+
+
+def summarize_trace(d, command):
+    """Markdown table of the library's kernels (and the probe); everything else the run launched (synthetic
+    data generation, torch copies, calibration set-up) is folded into one line."""
+    rows = _rows(d, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    other = [0, 0.0, 0.0]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].replace("|", "/")
+        if "jssa::" not in name and PROBE_KERNEL not in name:
+            other[0] += int(r["Calls"])
+            other[1] += float(r["TotalDurationNs"])
+            other[2] += float(r["Percentage"])
+            continue
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    if other[0]:
+        lines.append(f"| other kernels (set-up: data generation, copies) | {other[0]} | "
+                     f"{other[1] / other[0] / 1e3:.2f} | | | {other[2]:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+# ----------------------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama8b_128k")
-    ap.add_argument("--replicas", type=int, default=3)
-    ap.add_argument("--cpu-seqs", type=int, default=6, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--workload", default="llama8b_128k",
+                    help="llama8b_128k (default), llama8b_32k, hybrid_64k, mla_128k, tiny, tiny_mla")
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated per step (0: automatic)")
+    ap.add_argument("--cpu-seqs", type=int, default=-1,
+                    help="sequences in the CPU-oracle sample (0: skip; default 6 on the default workload)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="also run one 1 GiB device copy (reference kernel for counter scaling)")
+                    help="also run one elementwise kernel over 1 GiB (reference for counter scaling)")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--command", default="", help="profiling command recorded in a summary")
+    ap.add_argument("--out", help="summary output file")
     args = ap.parse_args()
+
+    if args.summarize_trace or args.summarize_counters:
+        if args.summarize_trace:
+            txt = summarize_trace(args.summarize_trace, args.command)
+        else:
+            from synth import WORKLOADS
+            w = WORKLOADS[args.workload]
+            score = layer_bytes(w, [w.seq_len] * w.batch, "sparse")["score"]
+            txt = json.dumps(summarize_counters(*args.summarize_counters, args.workload, score, args.command),
+                             indent=1) + "\n"
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(txt)
+        else:
+            print(txt)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the JSSA decode path is per-GPU and this build has no multi-GPU mode "
-              "(batch and KV heads would shard with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU: the JSSA decode path runs per GPU and has no multi-GPU mode here "
+              "(batch and KV heads would shard with no exchange inside the attention stage)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -196,69 +453,115 @@ def main():
     from synth import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    if w.kind != "gqa" or w.window:
-        print(f"workload {w.name}: bench times single-layer GQA workloads", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    seq = [w.seq_len] * w.batch
+    total_bytes, parts = step_bytes(w, seq, True)
+    full_bytes, _ = step_bytes(w, seq, False)
+    n_rep = args.replicas or (1 if total_bytes > (1 << 30) else 3)
+
     t_setup = time.perf_counter()
-    shape, M, case, reps, k_new, slot_new, bt, sl = setup(w, dev, args.replicas)
-    print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
-    q = case.layers[0].q
-    seq = [int(x) for x in case.seq_lens.cpu()]
+    shape, reps, bt, sl, case = setup(w, dev, n_rep)
+    print(f"[bench] {w.name}: setup {time.perf_counter() - t_setup:.1f} s, {n_rep} replica(s)", file=sys.stderr,
+          flush=True)
     ws = L.alloc_workspace(shape, dev)
     idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=dev)
-    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-    n_rep = len(reps)
+    out = torch.empty((w.batch, w.num_q_heads, w.v_dim), dtype=torch.bfloat16, device=dev)
+
+    def run_layer(lay, sparse):
+        if lay.window or not sparse:
+            L.jssa_full_decode(shape, lay.q, lay.kc, lay.vc, bt, sl, lay.window, w.sm_scale, out, ws)
+        else:
+            L.jssa_decode(shape, lay.q, lay.k_new, lay.slot_new, lay.M, lay.kp, lay.ks, lay.kc, lay.vc, bt, sl,
+                          idx, w.sm_scale, out, ws)
 
     def step(r):
-        kp, ks, kc, vc = reps[r]
-        L.jssa_decode(shape, q, k_new, slot_new, M, kp, ks, kc, vc, bt, sl, idx, w.sm_scale, out, ws)
+        for lay in reps[r]:
+            run_layer(lay, True)
 
     def full(r):
-        _, _, kc, vc = reps[r]
-        L.jssa_full_decode(shape, q, kc, vc, bt, sl, 0, w.sm_scale, out, ws)
+        for lay in reps[r]:
+            run_layer(lay, False)
 
-    ms, wall_ms = time_steps(step, args.steps, args.warmup, n_rep)
-    ms_full, _ = time_steps(full, max(10, args.steps // 10), max(2, args.warmup // 4), n_rep)
+    ms, med, p10, p90, wall_ms = time_steps(step, args.steps, args.warmup, n_rep)
+    print(f"[bench] eager {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    graph = None
+    if not args.no_graph:
+        g_ms, g_med, g_p10, g_p90 = time_graph(step, args.steps, args.warmup, n_rep)
+        graph = {"ms_per_step": round(g_ms, 5), "block_median_ms": round(g_med, 5), "p10_ms": round(g_p10, 5),
+                 "p90_ms": round(g_p90, 5), "steps_per_s": round(1e3 / g_ms, 2)}
+        print(f"[bench] graph {g_ms:.4f} ms/step", file=sys.stderr, flush=True)
+    ms_full, _, _, _, _ = time_steps(full, max(10, args.steps // 10), max(2, args.warmup // 4), n_rep)
+    print(f"[bench] full-KV {ms_full:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # stages of the first sparse layer (and the whole of a window layer, if any)
+    g0 = next(i for i, lay in enumerate(reps[0]) if not lay.window)
+
+    def lay_of(r):
+        return reps[r][g0]
+
+    def sel(stage):
+        return lambda r: L.jssa_select(shape, lay_of(r).q, lay_of(r).M, lay_of(r).kp, lay_of(r).ks, bt, sl, idx, ws,
+                                       stages=stage)
 
     stages = {
-        "store": lambda r: L.jssa_store(shape, k_new, slot_new, M, reps[r][0], reps[r][1], check_slots=False),
-        "select_prologue": lambda r: L.jssa_select(shape, q, M, reps[r][0], reps[r][1], bt, sl, idx, ws,
-                                                   stages=L.STAGE_PROLOGUE),
-        "select_stream": lambda r: L.jssa_select(shape, q, M, reps[r][0], reps[r][1], bt, sl, idx, ws,
-                                                 stages=L.STAGE_STREAM),
-        "select_finish": lambda r: L.jssa_select(shape, q, M, reps[r][0], reps[r][1], bt, sl, idx, ws,
-                                                 stages=L.STAGE_FINISH),
-        "attend": lambda r: L.jssa_attend(shape, q, reps[r][2], reps[r][3], bt, sl, idx, w.sm_scale, out, ws),
+        "store": lambda r: L.jssa_store(shape, lay_of(r).k_new, lay_of(r).slot_new, lay_of(r).M, lay_of(r).kp,
+                                        lay_of(r).ks, check_slots=False),
+        "select_prologue": sel(L.STAGE_PROLOGUE),
+        "select_stream": sel(L.STAGE_STREAM),
+        "select_finish": sel(L.STAGE_FINISH),
+        "attend": lambda r: L.jssa_attend(shape, lay_of(r).q, lay_of(r).kc, lay_of(r).vc, bt, sl, idx, w.sm_scale,
+                                          out, ws),
     }
+    win = [i for i, lay in enumerate(reps[0]) if lay.window]
+    if win:
+        stages["window_layer"] = lambda r: run_layer(reps[r][win[0]], True)
     for i in range(3):
         for f in stages.values():
             f(i % n_rep)
     stage_ms = time_stages(stages, args.steps, n_rep)
 
+    # achievable-bandwidth probe: torch's elementwise negation over 1 GiB (1 GiB read + 1 GiB written);
+    # with --copy-probe it runs once more alone, as the reference dispatch for counter scaling
+    src = torch.empty(PROBE_BYTES // 4, dtype=torch.float32, device=dev).normal_()
+    dst = torch.empty_like(src)
+    probe_ms = time_stages({"probe": lambda r: torch.neg(src, out=dst)}, 10, 1)["probe"]
     if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+    del src, dst
 
-    total_bytes, parts = algorithmic_bytes(w, seq, True)
-    full_bytes, _ = algorithmic_bytes(w, seq, False)
-    stream_bytes = parts["score"]
+    lb = layer_bytes(w, seq, "sparse")
+    stream_bytes = lb["score"]
     achieved = stream_bytes / (stage_ms["select_stream"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(stream_bytes),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(w.name),
                 "kernel": "select_stream (FP8 score stream + candidate compaction)",
                 "bytes_per_launch": stream_bytes, "avg_launch_ms": round(stage_ms["select_stream"], 5)}
 
-    cpu = None
-    if args.cpu_seqs > 0:
-        cpu = cpu_baseline(w, case, min(args.cpu_seqs, w.batch))
+    extra = {}
+    if w.kind == "mla":
+        fl = mla_attend_flops(w, seq, True)
+        att_s = stage_ms["attend"] * 1e-3
+        extra["mla_attend"] = {"flops": fl, "tflops": round(fl / att_s / 1e12, 1),
+                               "mfma_bf16_frac": round(fl / att_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "gbps": round((lb["selected_kv"] + lb["q_out_table"]) / att_s / 1e9, 1)}
+        ffl = mla_attend_flops(w, seq, False)
+        extra["mla_full"] = {"flops": ffl, "tflops": round(ffl / (ms_full * 1e-3) / 1e12, 1),
+                             "mfma_bf16_frac": round(ffl / (ms_full * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
+    n_cpu = args.cpu_seqs if args.cpu_seqs >= 0 else (6 if w.name == "llama8b_128k" else 0)
+    cpu = cpu_baseline(w, case, min(n_cpu, w.batch)) if n_cpu > 0 and not w.window else None
+
+    cfg = {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+           "head_dim": w.head_dim, "seq_len": w.seq_len, "page_size": w.page_size, "rank": w.rank,
+           "budget": w.budget, "kv_dtype": "bf16", "scoring_cache": "fp8 e4m3fn + fp32 scale per token",
+           "replicas": n_rep}
+    if w.window:
+        cfg.update(layers=w.num_layers, window=w.window, window_layers=list(w.window_layers()))
     res = {
-        "metric": "decode attn-stage steps/s @128K; HBM GB/s vs peak; speedup vs full-KV decode",
+        "metric": METRIC,
         "value": round(1e3 / ms, 2),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -270,21 +573,22 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded anisotropic keys/queries, 1% planted needles, random page permutation)",
-        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": w.seq_len,
-                   "page_size": w.page_size, "rank": w.rank, "budget": w.budget, "kv_dtype": "bf16",
-                   "scoring_cache": "fp8 e4m3fn + fp32 scale", "replicas": n_rep},
+        "config": cfg,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hbm_gbps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": total_bytes,
         "bytes_breakdown": parts,
+        "block_median_ms": round(med, 5), "p10_ms": round(p10, 5), "p90_ms": round(p90, 5),
+        "graph": graph,
+        "hbm_copy_probe_gbps": round(2 * PROBE_BYTES / (probe_ms * 1e-3) / 1e9, 1),
         "full_kv_ms_per_step": round(ms_full, 4),
         "full_kv_gbps": round(full_bytes / (ms_full * 1e-3) / 1e9, 1),
         "speedup_vs_full_kv": round(ms_full / ms, 3),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "host_wall_ms_per_step": round(wall_ms, 5),
+        **extra,
         "context": "pages' own figure: up to 6.43x end-to-end over full KV at 128K on one NVIDIA B200 "
                    "(MLA model, vLLM); not a target",
     }

@@ -169,7 +169,9 @@ int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
 /* jssa_full_decode — the dense baseline (README page §3, "Full-KV" decode):
  * the same attention over every position t < N (window == 0) or over the
  * last `window` positions [N - window, N) (window > 0: sliding-window layers,
- * which keep dense attention).  GQA only. */
+ * which keep dense attention).  MLA: keys are the 576-dim latent rows, values
+ * their first 512 dims (as in jssa_attend); out bf16 [batch, Hq, 512],
+ * v_cache ignored. */
 int32_t jssa_full_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
                          const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                          int32_t window, float sm_scale, uint16_t* out, float* lse_out,

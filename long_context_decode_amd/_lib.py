@@ -260,12 +260,13 @@ def jssa_decode(shape: Shape, q: torch.Tensor, k_new: Optional[torch.Tensor], sl
     _check("jssa_decode", _lib.jssa_decode(ctypes.byref(shape), *args, _stream()))
 
 
-def jssa_full_decode(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+def jssa_full_decode(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
                      block_table: torch.Tensor, seq_lens: torch.Tensor, window: int, sm_scale: float,
                      out: torch.Tensor, workspace: torch.Tensor, lse_out: Optional[torch.Tensor] = None) -> None:
     n, cs = _cache_shape(shape, k_cache)
     args = (_ptr("q", q, torch.bfloat16, (shape.batch, shape.num_q_heads, shape.head_dim)),
-            _ptr("k_cache", k_cache, torch.bfloat16, cs), _ptr("v_cache", v_cache, torch.bfloat16, cs),
+            _ptr("k_cache", k_cache, torch.bfloat16, cs),
+            _ptr("v_cache", v_cache, torch.bfloat16, cs, optional=shape.kind == KIND_MLA),
             *_table_args(shape, block_table, seq_lens), ctypes.c_int32(window), ctypes.c_float(sm_scale),
             _ptr("out", out, torch.bfloat16, (shape.batch, shape.num_q_heads, shape.v_dim)),
             _ptr("lse_out", lse_out, torch.float32, (shape.batch, shape.num_q_heads), optional=True),

@@ -24,6 +24,7 @@ struct Plan {
   int sp_splits, sp_len;     // sparse attention split plan
   int dn_splits, dn_len;     // dense (window 0) split plan
   int ml_splits, ml_len;     // MLA sparse attention split plan
+  int md_splits, md_len;     // MLA dense (window 0) split plan
   size_t off_qhat, off_tau, off_chunk, off_cand, off_part_o, off_part_ml, total;
 };
 
@@ -41,6 +42,20 @@ void split_plan(int64_t n_tok_max, int pairs, int* splits, int* len) {
   const int64_t l = cdiv(cdiv(n_tok_max, s), 256) * 256;
   *len = (int)l;
   *splits = (int)cdiv(n_tok_max, l);
+}
+
+// MLA dense split plan: about 512 blocks of (split, 32 heads, sequence), at
+// most 256 splits (the merge holds one split per thread), 64-row tiles.
+void mla_dense_plan(int64_t n, int batch, int Hq, int* splits, int* len) {
+  if (n <= 0) {
+    *splits = 1;
+    *len = 64;
+    return;
+  }
+  int64_t sp = cdiv(512, (int64_t)batch * std::max(1, Hq / 32));
+  sp = std::max<int64_t>(1, std::min<int64_t>({sp, cdiv(n, 64), 256}));
+  *len = (int)(cdiv(cdiv(n, sp), 64) * 64);
+  *splits = (int)cdiv(n, *len);
 }
 
 int32_t validate_shape(const jssa_shape* sh) {
@@ -96,8 +111,9 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
     sp = std::max<int64_t>(1, std::min<int64_t>({sp, cdiv(n, 64), 64}));
     p->ml_len = (int)(cdiv(cdiv(n, sp), 64) * 64);
     p->ml_splits = (int)cdiv(n, p->ml_len);
+    mla_dense_plan(p->maxN, p->batch, p->Hq, &p->md_splits, &p->md_len);
   }
-  const int max_splits = std::max({p->sp_splits, p->dn_splits, p->mla ? p->ml_splits : 1});
+  const int max_splits = std::max({p->sp_splits, p->dn_splits, p->mla ? std::max(p->ml_splits, p->md_splits) : 1});
   const size_t bh = (size_t)p->batch * p->Hkv;
   const size_t cand = bh * p->max_chunks * p->cp * p->P;   // one region per stream chunk
   size_t off = 0;
@@ -182,7 +198,6 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, int window,
                   float sm_scale, uint16_t* out, float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !out || !ws) return JSSA_ERR_NULL;
-  if (p.mla && !indices) return JSSA_ERR_UNSUPPORTED;       // dense MLA baseline not built
   if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
   if (window < 0) return JSSA_ERR_SHAPE;
   AttendArgs a{};
@@ -206,8 +221,15 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
   a.G = p.G;
   a.window = indices ? 0 : window;
   if (p.mla) {
-    a.splits = p.ml_splits;
-    a.split_len = p.ml_len;
+    if (indices) {
+      a.splits = p.ml_splits;
+      a.split_len = p.ml_len;
+    } else if (window > 0) {
+      mla_dense_plan(std::min<int64_t>(window, p.maxN), p.batch, p.Hq, &a.splits, &a.split_len);
+    } else {
+      a.splits = p.md_splits;
+      a.split_len = p.md_len;
+    }
     return hip_status(launch_mla_attend(a, stream));
   }
   if (indices) {
@@ -329,7 +351,6 @@ int32_t jssa_full_decode(const jssa_shape* shape, const uint16_t* q, const uint1
   Plan p;
   const int32_t st = make_plan(shape, &p);
   if (st != JSSA_OK) return st;
-  if (p.mla) return JSSA_ERR_UNSUPPORTED;
   return do_attend(p, q, k_cache, v_cache, block_table, seq_lens, nullptr, window, sm_scale, out, lse_out, workspace,
                    workspace_bytes, stream);
 }

@@ -23,6 +23,14 @@
 //     stored in that order.
 // The split's partial (unnormalised o, running max, running sum) goes to the
 // workspace and merge_kernel<512> combines the splits.
+//
+// DENSE instantiates the full-KV baseline over positions [lo, N) (lo = N - window
+// for a window, else 0) instead of an index list.
+//
+// Block order: the Hq/32 head blocks of one (split, sequence) read the same
+// rows.  Workgroups are dealt to the 8 XCDs round robin (workgroup L runs on
+// XCD L mod 8), so the linear block id is laid out to put those head blocks on
+// one XCD, one after another, where the later ones find the rows in its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -58,6 +66,7 @@ __device__ __forceinline__ int k_of_row(int t) { return (t & 32) + (t & 3) * 8 +
 
 }  // namespace
 
+template <bool DENSE>
 __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   __shared__ __align__(16) uint16_t Kt[kTile * kRow];
   __shared__ __align__(16) uint16_t Qs[kHB * kRow];
@@ -66,17 +75,25 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   __shared__ float red_l[4][kHB];
   __shared__ int rows[kTile];
 
-  const int s = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  const int HB = a.Hq / kHB;
+  const int L = (int)blockIdx.x;
+  const int rest = L >> 3, hb = rest % HB;
+  const int u = (rest / HB) * 8 + (L & 7);      // unit = (split, sequence)
+  if (u >= a.splits * a.batch) return;
+  const int s = u % a.splits, b = u / a.splits;
   const int tid = (int)threadIdx.x, l = lane_id(), w = tid >> 6;
   const int g = l >> 4, c = l & 15;
   int N = a.seq_lens[b];
   const int cap = a.max_pages * a.P;
   N = N < 0 ? 0 : (N > cap ? cap : N);
-  const int n_tok = N < a.B ? N : a.B;
+  int n_tok;
+  if (DENSE) n_tok = (a.window > 0 && N > a.window) ? a.window : N;
+  else n_tok = N < a.B ? N : a.B;
+  const int lo = N - n_tok;
   const int i0 = s * a.split_len;
   if (i0 >= n_tok) return;
   const int i1 = min(i0 + a.split_len, n_tok);
-  const int32_t* idx = a.indices + (int64_t)b * a.B;    // Hkv = 1
+  const int32_t* idx = DENSE ? nullptr : a.indices + (int64_t)b * a.B;    // Hkv = 1
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
   // Q of the 32 heads into LDS
@@ -106,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
       const int ii = t0 + tid;
       int r = -1;
       if (ii < i1) {
-        const int t = idx[ii];
+        const int t = DENSE ? lo + ii : idx[ii];
         if (t >= 0) r = bt[t / a.P] * a.P + (t % a.P);
       }
       rows[tid] = r;
@@ -209,7 +226,12 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
 }
 
 hipError_t launch_mla_attend(const AttendArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(mla_attend_kernel, dim3(a.splits, a.Hq / kHB, a.batch), dim3(kThreads), 0, s, a);
+  const int units = a.splits * a.batch;
+  const unsigned blocks = (unsigned)(((units + 7) / 8) * 8 * (a.Hq / kHB));
+  if (a.indices)
+    hipLaunchKernelGGL(mla_attend_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_attend_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_merge(a, kV, s);

@@ -18,7 +18,7 @@ from oracle import calibrate as ocal
 from oracle import fp8
 from oracle import gqa as ogqa
 from oracle import mla as omla
-from synth import WORKLOADS, bf16_bits, make_gqa_calibration, make_gqa_case, make_mla_case
+from synth import WORKLOADS, bf16_bits, make_gqa_calibration, make_gqa_case, make_mla_calibration, make_mla_case
 from synth.workloads import population_basis
 
 from util import (check_attention, check_codes, check_scores, check_selection, pack_kp, slots_for, unpack_kp)
@@ -510,3 +510,85 @@ def test_mla_decode_step():
         sel = gidx[b, 0][gidx[b, 0] >= 0]
         o, _ = omla.attend(q[b], rows[b][sel], w.sm_scale)
         check_attention(got[b], o)
+
+
+@pytest.mark.parametrize("name,window", [("tiny_mla", 0), ("mla_sampled", 0), ("mla_sampled", 1000)])
+def test_mla_full_decode_parity(name, window):
+    """Dense MLA baseline (all positions, or the last `window`) on the matrix cores."""
+    w, case, m32, rows, stored = _mla(name)
+    q = bf16_bits(case.q)
+    shape = L.shape_for(w)
+    out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    L.jssa_full_decode(shape, case.q.to(DEV), case.latent.to(DEV), None, case.block_table.to(DEV),
+                       case.seq_lens.to(DEV), window, w.sm_scale, out, L.alloc_workspace(shape), lse)
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(w.batch):
+        sel = ogqa.window_indices(int(case.seq_lens[b]), window)
+        o, l = omla.attend(q[b], rows[b][sel], w.sm_scale)
+        check_attention(got[b], o)
+        assert np.all(np.abs(glse[b] - l) <= 1e-3), np.abs(glse[b] - l).max()
+
+
+def test_mla_calibration_moments_and_basis():
+    """MLA: moments over the head-mean query's latent part and the cached latents, then the host basis."""
+    w = MLA_CASES["tiny_mla"]
+    shape = L.shape_for(w)
+    gq = torch.zeros((1, 512, 512), dtype=torch.float32, device=DEV)
+    gk = torch.zeros_like(gq)
+    chunks = list(make_mla_calibration(w, chunk=256))
+    ws = torch.empty(L.calib_workspace_bytes(shape, 256), dtype=torch.uint8, device=DEV)
+    T = 0
+    for qc, lat in chunks:
+        L.jssa_calib_moments(shape, qc.to(DEV), lat.to(DEV), gq, gk, ws)
+        T += qc.shape[0]
+    q64 = [(ocal.bf16_to_f64(bf16_bits(qc)), ocal.bf16_to_f64(bf16_bits(lat))) for qc, lat in chunks]
+    sq = sum(q.mean(axis=1)[:, :512].T @ q.mean(axis=1)[:, :512] for q, _ in q64) / T
+    sk = sum(r[:, :512].T @ r[:, :512] for _, r in q64) / T
+    gq_h, gk_h = gq.cpu().numpy()[0].astype(np.float64) / T, gk.cpu().numpy()[0].astype(np.float64) / T
+    for got, ref in ((gq_h, sq), (gk_h, sk)):
+        assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+    m = L.jssa_basis(shape, gq.cpu().numpy(), gk.cpu().numpy())[0].astype(np.float64)
+    mo = omla.calibrate(iter(q64), 512, w.rank)[0]
+    assert abs(ocal.l_marg(m.T @ m, sq, sk) - ocal.l_marg(mo.T @ mo, sq, sk)) < 1e-5
+
+
+def test_graph_replay_matches_eager():
+    """One decode step captured in a HIP graph replays bit-identically to the eager call, replay after replay."""
+    w, case, m32, rows_k, rows_v, stored = _gqa("mid_sampled")
+    shape, kp, ks, M = _upload(w, case, m32, stored)
+    bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
+    new_slot = torch.from_numpy(np.array([bt[b, (sl[b] - 1) // w.page_size] * w.page_size + (sl[b] - 1) % w.page_size
+                                          for b in range(w.batch)], np.int32)).to(DEV)
+    k_new = torch.from_numpy(np.stack([rows_k[b][-1] for b in range(w.batch)]).view(np.int16)).view(torch.bfloat16)
+    k_new = k_new.to(DEV)
+    lay = case.layers[0]
+    q, kc, vc = lay.q.to(DEV), lay.k_cache.to(DEV), lay.v_cache.to(DEV)
+    btd, sld = case.block_table.to(DEV), case.seq_lens.to(DEV)
+    ws = L.alloc_workspace(shape)
+    idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+
+    def step():
+        L.jssa_decode(shape, q, k_new, new_slot, M, kp, ks, kc, vc, btd, sld, idx, w.sm_scale, out, ws, lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (idx.clone(), out.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        idx.fill_(-7)
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0]), rep
+        assert torch.equal(out.view(torch.int16), ref[1].view(torch.int16)), rep
+        assert torch.equal(lse, ref[2]), rep
+        step()                                    # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0])
