@@ -44,12 +44,21 @@ __device__ __forceinline__ uint32_t f32_to_fp8(float x) {
 
 // ---------------------------------------------------------------- projection of a key row
 
-// y = sum_i m[i] * x[i] over din bf16 inputs (din % 8 == 0), one fp32 FMA
-// chain in index order.  jssa_store and the store fused into jssa_decode both
-// use it, so a key gets the same codes either way.
-__device__ __forceinline__ float project_row(const float* __restrict__ m, const uint16_t* __restrict__ x, int din) {
+// Projection of one bf16 row by one fp32 row of M, split over eight lanes:
+// project_part gives part p (0..7) of y = sum_i m[i] x[i], one fp32 FMA chain
+// over the dims [p din/8, (p+1) din/8) in index order (din % 64 == 0), and
+// proj_combine adds the parts of eight consecutive lanes (p = lane & 7) as
+// ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)), leaving the same value
+// in all eight (fp32 addition commutes).  jssa_store and the store fused into
+// jssa_decode both use this order, so a key gets the same codes either way.
+__device__ __forceinline__ float project_part(const float* __restrict__ m, const uint16_t* __restrict__ x, int din,
+                                              int part) {
+  const int len = din >> 3;
+  m += part * len;
+  x += part * len;
   float acc = 0.0f;
-  for (int i = 0; i < din; i += 8) {
+#pragma unroll 4
+  for (int i = 0; i < len; i += 8) {
     const uint4 kv = *reinterpret_cast<const uint4*>(x + i);
     const float4 m0 = *reinterpret_cast<const float4*>(m + i);
     const float4 m1 = *reinterpret_cast<const float4*>(m + i + 4);
@@ -63,6 +72,14 @@ __device__ __forceinline__ float project_row(const float* __restrict__ m, const 
     acc = __builtin_fmaf(m1.w, bf16_hi(kv.w), acc);
   }
   return acc;
+}
+
+// Every lane of the wavefront must execute this.
+__device__ __forceinline__ float proj_combine(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  return v;
 }
 
 // Byte offset of element o of the projected key at (page, head, slot) in the

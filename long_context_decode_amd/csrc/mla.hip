@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   __shared__ __align__(16) uint16_t Ps[kHB * kPRow];
   __shared__ float red_m[4][kHB];
   __shared__ float red_l[4][kHB];
-  __shared__ int rows[kTile];
+  __shared__ int rows[3][kTile];
 
   const int HB = a.Hq / kHB;
   const int L = (int)blockIdx.x;
@@ -93,15 +93,60 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   const int i0 = s * a.split_len;
   if (i0 >= n_tok) return;
   const int i1 = min(i0 + a.split_len, n_tok);
+  const int n_tiles = (i1 - i0 + kTile - 1) / kTile;
   const int32_t* idx = DENSE ? nullptr : a.indices + (int64_t)b * a.B;    // Hkv = 1
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  // Q of the 32 heads into LDS
-  for (int u = tid; u < kHB * (kD / 8); u += kThreads) {
-    const int m = u / (kD / 8), cc = u % (kD / 8);
-    *reinterpret_cast<uint4*>(&Qs[m * kRow + cc * 8]) =
-        *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + hb * kHB + m) * kD + cc * 8);
+  // physical rows of tile k (-1: none) into rows[buf]; threads 0..63
+  auto fill_rows = [&](int k, int buf) {
+    if (tid < kTile) {
+      const int ii = i0 + k * kTile + tid;
+      int r = -1;
+      if (ii < i1) {
+        const int t = DENSE ? lo + ii : idx[ii];
+        if (t >= 0) r = bt[t / a.P] * a.P + (t % a.P);
+      }
+      rows[buf][tid] = r;
+    }
+  };
+  // the tile's 64 x 72 16-byte pieces: 18 per thread, all loads in flight together
+  constexpr int kPieces = kTile * (kD / 8) / kThreads;   // 18
+  auto fetch = [&](int buf, uint4 (&reg)[kPieces]) {
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int q = tid + k * kThreads, tt = q / (kD / 8), cc = q % (kD / 8);
+      const int r = rows[buf][tt];
+      reg[k] = r >= 0 ? *reinterpret_cast<const uint4*>(a.k_cache + (int64_t)r * kD + cc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto put = [&](const uint4 (&reg)[kPieces]) {
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int q = tid + k * kThreads, tt = q / (kD / 8), cc = q % (kD / 8);
+      *reinterpret_cast<uint4*>(&Kt[tt * kRow + cc * 8]) = reg[k];
+    }
+  };
+
+  fill_rows(0, 0);
+  fill_rows(1, 1);
+  // Q of the 32 heads into LDS (9 pieces per thread, loads together)
+  {
+    constexpr int kQ = kHB * (kD / 8) / kThreads;        // 9
+    uint4 qv[kQ];
+#pragma unroll
+    for (int k = 0; k < kQ; ++k) {
+      const int q = tid + k * kThreads, m = q / (kD / 8), cc = q % (kD / 8);
+      qv[k] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + hb * kHB + m) * kD + cc * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < kQ; ++k) {
+      const int q = tid + k * kThreads, m = q / (kD / 8), cc = q % (kD / 8);
+      *reinterpret_cast<uint4*>(&Qs[m * kRow + cc * 8]) = qv[k];
+    }
   }
+  __syncthreads();
+  uint4 reg[kPieces];
+  fetch(0, reg);
 
   // lane state: heads mt*16 + 4g + j (mt = 0, 1; j = 0..3)
   float m_run[2][4], l_run[2][4];
@@ -117,26 +162,13 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
     for (int nt = 0; nt < 8; ++nt) O[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  for (int t0 = i0; t0 < i1; t0 += kTile) {
-    __syncthreads();                                   // previous tile fully consumed
-    if (tid < kTile) {
-      const int ii = t0 + tid;
-      int r = -1;
-      if (ii < i1) {
-        const int t = DENSE ? lo + ii : idx[ii];
-        if (t >= 0) r = bt[t / a.P] * a.P + (t % a.P);
-      }
-      rows[tid] = r;
-    }
+  for (int k = 0; k < n_tiles; ++k) {
+    __syncthreads();                                   // previous tile consumed; rows[(k+1)%3] written
+    put(reg);
+    if (k + 2 < n_tiles) fill_rows(k + 2, (k + 2) % 3);
     __syncthreads();
-    for (int u = tid; u < kTile * (kD / 8); u += kThreads) {
-      const int tt = u / (kD / 8), cc = u % (kD / 8);
-      const int r = rows[tt];
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r >= 0) v = *reinterpret_cast<const uint4*>(a.k_cache + (int64_t)r * kD + cc * 8);
-      *reinterpret_cast<uint4*>(&Kt[tt * kRow + cc * 8]) = v;
-    }
-    __syncthreads();
+    if (k + 1 < n_tiles) fetch((k + 1) % 3, reg);      // next tile's loads overlap this tile's math
+    const int* trow = rows[k % 3];
 
     // ---- S = Q K^T for rows [16w, 16w + 16)
     f32x4 S[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -149,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
         S[mt] = mfma16(aq, bk, S[mt]);
       }
     }
-    const bool valid = rows[w * 16 + c] >= 0;
+    const bool valid = trow[w * 16 + c] >= 0;
     float x[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)

@@ -184,6 +184,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   constexpr int TPT = R >= 8 ? 1 : 8 / R;      // sampled tokens per thread with loads in flight together
   const int h = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
   __shared__ double qbar[kMlaLatent + kMlaRope];
+  __shared__ double qpart[8 * (kMlaLatent + kMlaRope)];   // head-group partials of qbar (G <= 128)
   __shared__ float qh[S];
   __shared__ float ynew[S];
   __shared__ uint32_t skeys[kSampleMax];
@@ -238,25 +239,56 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   };
   if (sampled) issue_pages(0);
 
-  // qbar: mean of the G query heads of KV head h (fp64)
-  for (int i = tid; i < din; i += kPrologueThreads) {
-    double s = 0.0;
-    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + (int64_t)h * a.G) * din + i;
-    for (int g0 = 0; g0 < a.G; g0 += 8) {      // eight heads' loads in flight, summed in head order
-      float v[8];
+  // qbar: mean of the G query heads of KV head h (fp64).  Heads go in groups
+  // of up to 16; a thread sums one group's heads over 8 dims (wide loads, all
+  // in flight), then the group partials are added in group order.
+  {
+    const int hg = a.G < 16 ? a.G : 16;
+    const int groups = a.G / hg;
+    const int chunks = din >> 3;
+    for (int u = tid; u < groups * chunks; u += kPrologueThreads) {
+      const int grp = u / chunks, c = u % chunks;
+      const uint16_t* qp = a.q + ((int64_t)b * a.Hq + (int64_t)h * a.G + grp * hg) * din + c * 8;
+      uint4 v[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = g0 + j < a.G ? bf16_to_f32(qp[(int64_t)(g0 + j) * din]) : 0.0f;
+      for (int j = 0; j < 16; ++j)
+        if (j < hg) v[j] = *reinterpret_cast<const uint4*>(qp + (int64_t)j * din);
+      double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += (double)v[j];
+      for (int j = 0; j < 16; ++j) {
+        if (j < hg) {
+          acc[0] += (double)bf16_lo(v[j].x);
+          acc[1] += (double)bf16_hi(v[j].x);
+          acc[2] += (double)bf16_lo(v[j].y);
+          acc[3] += (double)bf16_hi(v[j].y);
+          acc[4] += (double)bf16_lo(v[j].z);
+          acc[5] += (double)bf16_hi(v[j].z);
+          acc[6] += (double)bf16_lo(v[j].w);
+          acc[7] += (double)bf16_hi(v[j].w);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qpart[grp * din + c * 8 + k] = acc[k];
     }
-    qbar[i] = s / (double)a.G;
+    __syncthreads();
+    for (int i = tid; i < din; i += kPrologueThreads) {
+      double acc = 0.0;
+      for (int g = 0; g < groups; ++g) acc += qpart[g * din + i];
+      qbar[i] = acc / (double)a.G;
+    }
   }
   if (sampled) issue_rows();
-  // the new token of this sequence (jssa_decode): projected exactly as jssa_store does
+  // the new token of this sequence (jssa_decode): projected exactly as
+  // jssa_store does (eight threads per output, project_part / proj_combine)
   const int new_slot = a.k_new ? a.slot_new[b] : -1;
-  if (new_slot >= 0 && tid < S) {
+  if (new_slot >= 0) {
     const uint16_t* row = a.mla ? a.k_new + (int64_t)b * din : a.k_new + ((int64_t)b * a.Hkv + h) * a.d;
-    ynew[tid] = tid < a.r ? project_row(Mh + (int64_t)tid * dm, row, dm) : bf16_to_f32(row[kMlaLatent + (tid - a.r)]);
+    const int o = tid >> 3, part = tid & 7;
+    float v = 0.0f;
+    if (o < a.r) v = project_part(Mh + (int64_t)o * dm, row, dm, part);
+    v = proj_combine(v);
+    if (o < a.r && part == 0) ynew[o] = v;
+    if (a.mla && tid < kMlaRope) ynew[a.r + tid] = bf16_to_f32(row[kMlaLatent + tid]);
   }
   __syncthreads();
   // qhat = M qbar (MLA: [M qbar[:512] ; qbar[512:]]) in fp64, rounded once to
@@ -265,20 +297,24 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     const int o = tid >> 3, part = tid & 7;
     double v = 0.0;
     if (o < a.r) {
-      const int len = dm / 8;
+      const int len = dm / 8;                 // 16, 32 or 64: all of this thread's M loads go out at once
       const float* m = Mh + (int64_t)o * dm + part * len;
       const double* qb = qbar + part * len;
-      for (int i = 0; i < len; i += 8) {
-        const float4 m0 = *reinterpret_cast<const float4*>(m + i);
-        const float4 m1 = *reinterpret_cast<const float4*>(m + i + 4);
-        v = __builtin_fma((double)m0.x, qb[i], v);
-        v = __builtin_fma((double)m0.y, qb[i + 1], v);
-        v = __builtin_fma((double)m0.z, qb[i + 2], v);
-        v = __builtin_fma((double)m0.w, qb[i + 3], v);
-        v = __builtin_fma((double)m1.x, qb[i + 4], v);
-        v = __builtin_fma((double)m1.y, qb[i + 5], v);
-        v = __builtin_fma((double)m1.z, qb[i + 6], v);
-        v = __builtin_fma((double)m1.w, qb[i + 7], v);
+      for (int k0 = 0; k0 < len; k0 += 32) {  // 32 dims (8 loads) in flight per batch
+        float4 mv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k0 + k * 4 < len) mv[k] = *reinterpret_cast<const float4*>(m + k0 + k * 4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k0 + k * 4 < len) {
+            const double* qq = qb + k0 + k * 4;
+            v = __builtin_fma((double)mv[k].x, qq[0], v);
+            v = __builtin_fma((double)mv[k].y, qq[1], v);
+            v = __builtin_fma((double)mv[k].z, qq[2], v);
+            v = __builtin_fma((double)mv[k].w, qq[3], v);
+          }
+        }
       }
     }
     v += __shfl_xor(v, 1);
@@ -312,6 +348,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   } else {
     uint32_t valid = 0;
     for (int u0 = 0; u0 < ns; u0 += kPrologueThreads * TPT) {
+      asm volatile("" ::: "memory");     // qh is re-read from LDS each round, not held in registers
       if (u0 > 0) {
         issue_pages(u0);
         issue_rows();

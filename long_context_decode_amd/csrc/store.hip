@@ -3,52 +3,62 @@
 // scoring cache (paper summary page, §3.4 Projected Scoring Cache:
 // K_proj = K M^T kept in FP8; MLA scores on 64 latent + 64 RoPE dims).
 //
-// One wavefront per (new token, KV head).  Lane o computes output o (and
-// o + 64 for the 128-dim MLA representation) with one fp32 FMA chain over the
-// input dims; the per-token absmax is a wave max; codes are written into the
+// One wavefront per (new token, KV head).  The projected outputs are done
+// eight at a time: lane l takes part l & 7 of output 8 pass + (l >> 3)
+// (project_part / proj_combine); the MLA RoPE dims pass through, one per
+// lane.  The per-token absmax is a wave max; codes are written into the
 // piece-major (page, head) block: byte (i/16)*page*16 + slot*16 + i%16.
 #include "common.h"
 #include "kernels.h"
 
 namespace jssa {
 
+namespace {
+constexpr int kMaxPasses = 16;   // r <= 128
+}
+
 __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
   const int wave = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int lane = lane_id();
   const int t = wave / a.Hkv, h = wave % a.Hkv;
-  if (t >= a.T) return;
+  if (t >= a.T) return;                               // uniform per wavefront
   const int sl = a.slot[t];
   if (sl < 0) return;
   const int page = sl / a.P, sip = sl % a.P;
+  const int oi = lane >> 3, part = lane & 7;
 
-  // input row (bf16) and the rows of M this lane needs
   const uint16_t* row = a.mla ? a.k_new + (int64_t)t * (kMlaLatent + kMlaRope)
                               : a.k_new + ((int64_t)t * a.Hkv + h) * a.d;
   const int din = a.mla ? kMlaLatent : a.d;
-  float y[2] = {0.0f, 0.0f};
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int o = lane + 64 * k;
-    if (o < a.r) {
-      y[k] = project_row(a.M + ((int64_t)(a.mla ? 0 : h) * a.r + o) * din, row, din);
-    } else if (a.mla && o < a.S) {
-      y[k] = bf16_to_f32(row[kMlaLatent + (o - a.r)]);   // RoPE dims pass through
-    }
-  }
+  const float* Mh = a.M + (int64_t)(a.mla ? 0 : h) * a.r * din;
+  const int passes = a.r >> 3;
+  float y[kMaxPasses];
   float amax = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
-    if (lane + 64 * k < a.S) amax = fmaxf(amax, fabsf(y[k]));
+  for (int p = 0; p < kMaxPasses; ++p) {
+    if (p < passes) {
+      y[p] = proj_combine(project_part(Mh + (int64_t)(p * 8 + oi) * din, row, din, part));
+      amax = fmaxf(amax, fabsf(y[p]));
+    }
+  }
+  float yr = 0.0f;
+  if (a.mla) {                                        // RoPE dims: lane l -> output r + l
+    yr = bf16_to_f32(row[kMlaLatent + lane]);
+    amax = fmaxf(amax, fabsf(yr));
+  }
   amax = wave_max(amax);
   const float scale = amax / 448.0f;
 
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int o = lane + 64 * k;
-    if (o < a.S) {
-      const uint32_t code = (scale > 0.0f) ? f32_to_fp8(y[k] / scale) : 0u;
-      a.kp[kp_offset(page, h, sip, o, a.Hkv, a.S, a.P)] = (uint8_t)code;
+  for (int p = 0; p < kMaxPasses; ++p) {
+    if (p < passes && part == 0) {
+      const uint32_t code = (scale > 0.0f) ? f32_to_fp8(y[p] / scale) : 0u;
+      a.kp[kp_offset(page, h, sip, p * 8 + oi, a.Hkv, a.S, a.P)] = (uint8_t)code;
     }
+  }
+  if (a.mla) {
+    const uint32_t code = (scale > 0.0f) ? f32_to_fp8(yr / scale) : 0u;
+    a.kp[kp_offset(page, h, sip, a.r + lane, a.Hkv, a.S, a.P)] = (uint8_t)code;
   }
   if (lane == 0) a.kp_scale[((int64_t)page * a.Hkv + h) * a.P + sip] = scale;
 }
