@@ -494,11 +494,13 @@ def main():
     ms_full, _, _, _, _ = time_steps(full, max(10, args.steps // 10), max(2, args.warmup // 4), n_rep)
     print(f"[bench] full-KV {ms_full:.4f} ms/step", file=sys.stderr, flush=True)
 
-    # stages of the first sparse layer (and the whole of a window layer, if any)
-    g0 = next(i for i, lay in enumerate(reps[0]) if not lay.window)
+    # stages of the sparse layers, rotating over (replica, layer) so that no launch finds the previous
+    # launch's bytes in the Infinity Cache (and the whole of a window layer, if any)
+    units = [(r, i) for r in range(n_rep) for i, lay in enumerate(reps[r]) if not lay.window]
 
-    def lay_of(r):
-        return reps[r][g0]
+    def lay_of(k):
+        r, i = units[k % len(units)]
+        return reps[r][i]
 
     def sel(stage):
         return lambda r: L.jssa_select(shape, lay_of(r).q, lay_of(r).M, lay_of(r).kp, lay_of(r).ks, bt, sl, idx, ws,
@@ -513,13 +515,14 @@ def main():
         "attend": lambda r: L.jssa_attend(shape, lay_of(r).q, lay_of(r).kc, lay_of(r).vc, bt, sl, idx, w.sm_scale,
                                           out, ws),
     }
-    win = [i for i, lay in enumerate(reps[0]) if lay.window]
+    win = [(r, i) for r in range(n_rep) for i, lay in enumerate(reps[r]) if lay.window]
     if win:
-        stages["window_layer"] = lambda r: run_layer(reps[r][win[0]], True)
+        stages["window_layer"] = lambda k: run_layer(reps[win[k % len(win)][0]][win[k % len(win)][1]], True)
+    n_units = max(len(units), len(win))
     for i in range(3):
         for f in stages.values():
-            f(i % n_rep)
-    stage_ms = time_stages(stages, args.steps, n_rep)
+            f(i)
+    stage_ms = time_stages(stages, args.steps, n_units)
 
     # achievable-bandwidth probe: torch's elementwise negation over 1 GiB (1 GiB read + 1 GiB written);
     # with --copy-probe it runs once more alone, as the reference dispatch for counter scaling

@@ -592,3 +592,74 @@ def test_graph_replay_matches_eager():
         step()                                    # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(idx, ref[0])
+
+
+def test_hybrid_stack_layers_in_sequence():
+    """A 4-layer sliding-window / global stack run back to back like one step: window layers through
+    jssa_full_decode, global layers through jssa_decode with their own basis M (per layer, per KV head)."""
+    w = _w("hybrid_64k", name="hyb", model="test", batch=2, num_q_heads=8, num_kv_heads=4, seq_len=6000,
+           budget=512, num_layers=4, window=512, calib_seqs=2, calib_len=1024)
+    case = make_gqa_case(w, ragged=True)
+    shape = L.shape_for(w)
+    bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
+    btd, sld = case.block_table.to(DEV), case.seq_lens.to(DEV)
+    ws = L.alloc_workspace(shape)
+    new_slot = np.array([bt[b, (sl[b] - 1) // w.page_size] * w.page_size + (sl[b] - 1) % w.page_size
+                         for b in range(w.batch)], np.int32)
+    host, dev_out = {}, {}
+    for l, lay in sorted(case.layers.items()):
+        kc, vc = bf16_bits(lay.k_cache), bf16_bits(lay.v_cache)
+        rows_k = [ogqa.logical_rows(kc, bt[b], int(sl[b]), w.page_size) for b in range(w.batch)]
+        rows_v = [ogqa.logical_rows(vc, bt[b], int(sl[b]), w.page_size) for b in range(w.batch)]
+        out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+        if l in w.window_layers():
+            L.jssa_full_decode(shape, lay.q.to(DEV), lay.k_cache.to(DEV), lay.v_cache.to(DEV), btd, sld, w.window,
+                               w.sm_scale, out, ws)
+            host[l] = (rows_k, rows_v, None, None)
+            dev_out[l] = (out, None, None, None)
+            continue
+        q, k = make_gqa_calibration(w, l)
+        m32 = ocal.calibrate(ocal.bf16_to_f64(bf16_bits(q)), ocal.bf16_to_f64(bf16_bits(k)), w.group,
+                             w.rank).astype(np.float32)
+        stored = [ogqa.store(rk, m32) for rk in rows_k]
+        prev = [(c.copy(), s.copy()) for c, s in stored]
+        for b in range(w.batch):                  # the newest token is stored by jssa_decode itself
+            prev[b][0][-1] = 0
+            prev[b][1][-1] = 0
+        kp, ks = pack_kp([c for c, _ in prev], [s for _, s in prev], bt, w.page_size, lay.k_cache.shape[0], sl)
+        kp, ks = torch.from_numpy(kp).to(DEV), torch.from_numpy(ks).to(DEV)
+        k_new = torch.from_numpy(np.stack([rows_k[b][-1] for b in range(w.batch)]).view(np.int16)).view(torch.bfloat16)
+        idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=DEV)
+        L.jssa_decode(shape, lay.q.to(DEV), k_new.to(DEV), torch.from_numpy(new_slot).to(DEV),
+                      torch.from_numpy(m32).to(DEV), kp, ks, lay.k_cache.to(DEV), lay.v_cache.to(DEV), btd, sld, idx,
+                      w.sm_scale, out, ws)
+        host[l] = (rows_k, rows_v, m32, stored)
+        dev_out[l] = (out, idx, kp, ks)
+    torch.cuda.synchronize()
+    for l, lay in sorted(case.layers.items()):
+        rows_k, rows_v, m32, stored = host[l]
+        out, idx, kp, ks = dev_out[l]
+        got = out.float().cpu().numpy()
+        q = bf16_bits(lay.q)
+        if m32 is None:
+            for b in range(w.batch):
+                sel = ogqa.window_indices(int(sl[b]), w.window)
+                for h in range(w.num_kv_heads):
+                    j0 = h * w.group
+                    o, _ = ogqa.attend_group(q[b, j0:j0 + w.group], rows_k[b][:, h], rows_v[b][:, h], sel, w.sm_scale)
+                    check_attention(got[b, j0:j0 + w.group], o)
+            continue
+        kp_h, ks_h, gidx = kp.cpu().numpy(), ks.cpu().numpy(), idx.cpu().numpy()
+        for b in range(w.batch):
+            n = int(sl[b])
+            c, s = unpack_kp(kp_h, ks_h, bt[b], n, w.page_size)
+            check_codes(c[-1], stored[b][0][-1], max_frac=1.0 / 8)
+            qbar_hat = ogqa.project_query(q[b], m32, w.group)
+            for h in range(w.num_kv_heads):
+                sc = ogqa.scores(qbar_hat[h], c[:, h], s[:, h])
+                oidx, tau = ogqa.select_topb(sc, w.budget)
+                check_selection(gidx[b, h], oidx, sc, tau)
+                j0 = h * w.group
+                o, _ = ogqa.attend_group(q[b, j0:j0 + w.group], rows_k[b][:, h], rows_v[b][:, h], gidx[b, h],
+                                         w.sm_scale)
+                check_attention(got[b, j0:j0 + w.group], o)
