@@ -46,19 +46,18 @@ __device__ __forceinline__ uint32_t f32_to_fp8(float x) {
 
 // Projection of one bf16 row by one fp32 row of M, split over eight lanes:
 // project_part gives part p (0..7) of y = sum_i m[i] x[i], one fp32 FMA chain
-// over the dims [p din/8, (p+1) din/8) in index order (din % 64 == 0), and
-// proj_combine adds the parts of eight consecutive lanes (p = lane & 7) as
-// ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)), leaving the same value
-// in all eight (fp32 addition commutes).  jssa_store and the store fused into
-// jssa_decode both use this order, so a key gets the same codes either way.
+// over the 8-element chunks c = p, p + 8, p + 16, ... in order (din % 64 == 0;
+// at each step the eight parts read eight consecutive chunks, 256 contiguous
+// bytes of m), and proj_combine adds the parts of eight consecutive lanes
+// (p = lane & 7) as ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)), leaving
+// the same value in all eight (fp32 addition commutes).  jssa_store and the
+// store fused into jssa_decode both use this order, so a key gets the same
+// codes either way.
 __device__ __forceinline__ float project_part(const float* __restrict__ m, const uint16_t* __restrict__ x, int din,
                                               int part) {
-  const int len = din >> 3;
-  m += part * len;
-  x += part * len;
   float acc = 0.0f;
 #pragma unroll 4
-  for (int i = 0; i < len; i += 8) {
+  for (int i = part * 8; i < din; i += 64) {
     const uint4 kv = *reinterpret_cast<const uint4*>(x + i);
     const float4 m0 = *reinterpret_cast<const float4*>(m + i);
     const float4 m1 = *reinterpret_cast<const float4*>(m + i + 4);

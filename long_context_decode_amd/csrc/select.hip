@@ -107,9 +107,13 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k
 // kDigitBits bits per pass: every thread adds its keys to an LDS histogram,
 // wave 0 finds the digit; two block barriers per pass (the histogram of the
 // next pass is cleared during the current one).  hist2 holds 2 * kHistWords words.
+//
+// With stop_shift > 0 the digits below bit stop_shift are not resolved: *kth
+// is then the lower edge (low bits zero) of the bin holding the k-th key, a
+// bound <= the k-th key, and *need is not meaningful.
 template <int NT>
 __device__ void block_radix_select(const uint32_t* keys, int n, uint32_t k, uint32_t* hist2, uint32_t* tmp,
-                                   uint32_t* kth, uint32_t* need) {
+                                   uint32_t* kth, uint32_t* need, int stop_shift = 0) {
   const int tid = (int)threadIdx.x;
   for (int i = tid; i < kHistWords; i += NT) hist2[i] = 0u;
   const uint32_t ref = keys[0];
@@ -140,7 +144,7 @@ __device__ void block_radix_select(const uint32_t* keys, int n, uint32_t k, uint
     k = tmp[49];
     hi_mask = ~((1u << shift) - 1u);
     prefix &= hi_mask;
-    if (shift == 0) break;
+    if (shift <= stop_shift) break;
     hb = shift - 1;
   }
   *kth = prefix;
@@ -188,6 +192,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   __shared__ float qh[S];
   __shared__ float ynew[S];
   __shared__ uint32_t skeys[kSampleMax];
+  __shared__ int32_t sph[kSampleMax];                      // physical page of each sampled token, -1: none
   __shared__ __align__(16) uint32_t hist[2 * kHistWords];
   __shared__ uint32_t tmp[64];
   const int64_t bh = (int64_t)b * a.Hkv + h;
@@ -195,6 +200,22 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   const int din = a.mla ? kMlaLatent + kMlaRope : a.d;
   const int dm = a.mla ? kMlaLatent : a.d;
   const float* Mh = a.M + (int64_t)(a.mla ? 0 : h) * a.r * dm;
+
+  // qbar loads go out first, beside the sequence-length load: heads in groups
+  // of up to 16, a thread takes one group's heads over 8 dims (groups x
+  // chunks <= 8 x 72 units, so one unit per thread)
+  const int hg = a.G < 16 ? a.G : 16;
+  const int groups = a.G / hg;
+  const int chunks = din >> 3;
+  const bool qact = tid < groups * chunks;
+  const int qgrp = tid / chunks, qc = tid % chunks;
+  uint4 qv[16];
+  if (qact) {
+    const uint16_t* qp = a.q + ((int64_t)b * a.Hq + (int64_t)h * a.G + qgrp * hg) * din + qc * 8;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < hg) qv[j] = *reinterpret_cast<const uint4*>(qp + (int64_t)j * din);
+  }
 
   // sample plan: a strided set of whole pages; tau will be the ks-th largest
   // sampled key with ks / sample = target / N, target = min(2B, cap/2)
@@ -211,73 +232,62 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   }
   const int ns = sp * a.P;
   // sample loads go out in two steps around the query work: the block-table
-  // entries first (with the query loads), the FP8 rows before the projection
+  // entries of every round first (with the query loads), then each round's
+  // FP8 rows (round 0 before the projection).  Round r covers the sample
+  // indices u = (r TPT + j) threads + tid, j < TPT.
   uint4 pc[TPT][R];
   float sc[TPT];
-  int tt[TPT];
-  int64_t ph[TPT];
-  auto issue_pages = [&](int u0) {
+  if (sampled) {                               // all loads first, then the LDS stores
+    constexpr int KS = kSampleMax / kPrologueThreads;
+    int ph[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int u = k * kPrologueThreads + tid;
+      ph[k] = -1;
+      if (u < ns) {
+        const int pl = (int)(((int64_t)(u / a.P) * n_pages) / sp);
+        if (pl * a.P + u % a.P < N) ph[k] = a.block_table[(int64_t)b * a.max_pages + pl];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k)               // each thread reads back only its own entries
+      if (k * kPrologueThreads + tid < ns) sph[k * kPrologueThreads + tid] = ph[k];
+  }
+  auto issue_rows = [&](int r) {
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
-      const int u = u0 + j * kPrologueThreads + tid;
-      tt[j] = -1;
-      if (u < ns) {
-        const int i = u / a.P, slot = u % a.P;
-        const int pl = (int)(((int64_t)i * n_pages) / sp);
-        const int t = pl * a.P + slot;
-        if (t < N) {
-          tt[j] = t;
-          ph[j] = a.block_table[(int64_t)b * a.max_pages + pl];
-        }
-      }
+      const int u = (r * TPT + j) * kPrologueThreads + tid;
+      if (u < ns && sph[u] >= 0) load_token<R>(a, sph[u], h, u % a.P, pc[j], sc[j]);
     }
   };
-  auto issue_rows = [&]() {
-#pragma unroll
-    for (int j = 0; j < TPT; ++j)
-      if (tt[j] >= 0) load_token<R>(a, ph[j], h, tt[j] % a.P, pc[j], sc[j]);
-  };
-  if (sampled) issue_pages(0);
 
-  // qbar: mean of the G query heads of KV head h (fp64).  Heads go in groups
-  // of up to 16; a thread sums one group's heads over 8 dims (wide loads, all
-  // in flight), then the group partials are added in group order.
-  {
-    const int hg = a.G < 16 ? a.G : 16;
-    const int groups = a.G / hg;
-    const int chunks = din >> 3;
-    for (int u = tid; u < groups * chunks; u += kPrologueThreads) {
-      const int grp = u / chunks, c = u % chunks;
-      const uint16_t* qp = a.q + ((int64_t)b * a.Hq + (int64_t)h * a.G + grp * hg) * din + c * 8;
-      uint4 v[16];
+  // qbar: mean of the G query heads of KV head h (fp64): per dim the group's
+  // heads in order, then the group partials in group order
+  if (qact) {
+    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < hg) v[j] = *reinterpret_cast<const uint4*>(qp + (int64_t)j * din);
-      double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j < hg) {
-          acc[0] += (double)bf16_lo(v[j].x);
-          acc[1] += (double)bf16_hi(v[j].x);
-          acc[2] += (double)bf16_lo(v[j].y);
-          acc[3] += (double)bf16_hi(v[j].y);
-          acc[4] += (double)bf16_lo(v[j].z);
-          acc[5] += (double)bf16_hi(v[j].z);
-          acc[6] += (double)bf16_lo(v[j].w);
-          acc[7] += (double)bf16_hi(v[j].w);
-        }
+    for (int j = 0; j < 16; ++j) {
+      if (j < hg) {
+        acc[0] += (double)bf16_lo(qv[j].x);
+        acc[1] += (double)bf16_hi(qv[j].x);
+        acc[2] += (double)bf16_lo(qv[j].y);
+        acc[3] += (double)bf16_hi(qv[j].y);
+        acc[4] += (double)bf16_lo(qv[j].z);
+        acc[5] += (double)bf16_hi(qv[j].z);
+        acc[6] += (double)bf16_lo(qv[j].w);
+        acc[7] += (double)bf16_hi(qv[j].w);
       }
+    }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) qpart[grp * din + c * 8 + k] = acc[k];
-    }
-    __syncthreads();
-    for (int i = tid; i < din; i += kPrologueThreads) {
-      double acc = 0.0;
-      for (int g = 0; g < groups; ++g) acc += qpart[g * din + i];
-      qbar[i] = acc / (double)a.G;
-    }
+    for (int k = 0; k < 8; ++k) qpart[qgrp * din + qc * 8 + k] = acc[k];
   }
-  if (sampled) issue_rows();
+  __syncthreads();
+  for (int i = tid; i < din; i += kPrologueThreads) {
+    double acc = 0.0;
+    for (int g = 0; g < groups; ++g) acc += qpart[g * din + i];
+    qbar[i] = acc / (double)a.G;
+  }
+  if (sampled) issue_rows(0);
   // the new token of this sequence (jssa_decode): projected exactly as
   // jssa_store does (eight threads per output, project_part / proj_combine)
   const int new_slot = a.k_new ? a.slot_new[b] : -1;
@@ -292,23 +302,25 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   }
   __syncthreads();
   // qhat = M qbar (MLA: [M qbar[:512] ; qbar[512:]]) in fp64, rounded once to
-  // fp32: 8 threads per output, each one eighth of the dims, fixed xor order
+  // fp32: 8 threads per output, thread p taking the float4 groups p, p + 8,
+  // ... (the 8 threads of an output read 128 contiguous bytes per step), partial
+  // sums added in a fixed xor order
   {
     const int o = tid >> 3, part = tid & 7;
     double v = 0.0;
     if (o < a.r) {
-      const int len = dm / 8;                 // 16, 32 or 64: all of this thread's M loads go out at once
-      const float* m = Mh + (int64_t)o * dm + part * len;
-      const double* qb = qbar + part * len;
-      for (int k0 = 0; k0 < len; k0 += 32) {  // 32 dims (8 loads) in flight per batch
+      const int nf = dm / 32;                 // float4 groups per thread: 4, 8 or 16
+      const float* m = Mh + (int64_t)o * dm + part * 4;
+      const double* qb = qbar + part * 4;
+      for (int k0 = 0; k0 < nf; k0 += 8) {     // 8 loads in flight per batch
         float4 mv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (k0 + k * 4 < len) mv[k] = *reinterpret_cast<const float4*>(m + k0 + k * 4);
+          if (k0 + k < nf) mv[k] = *reinterpret_cast<const float4*>(m + (k0 + k) * 32);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          if (k0 + k * 4 < len) {
-            const double* qq = qb + k0 + k * 4;
+          if (k0 + k < nf) {
+            const double* qq = qb + (k0 + k) * 32;
             v = __builtin_fma((double)mv[k].x, qq[0], v);
             v = __builtin_fma((double)mv[k].y, qq[1], v);
             v = __builtin_fma((double)mv[k].z, qq[2], v);
@@ -346,34 +358,27 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   } else if (!sampled) {
     tau = 0u;                            // every token is a candidate
   } else {
-    uint32_t valid = 0;
-    for (int u0 = 0; u0 < ns; u0 += kPrologueThreads * TPT) {
+    for (int r = 0; r * TPT * kPrologueThreads < ns; ++r) {
       asm volatile("" ::: "memory");     // qh is re-read from LDS each round, not held in registers
-      if (u0 > 0) {
-        issue_pages(u0);
-        issue_rows();
-      }
+      if (r > 0) issue_rows(r);
 #pragma unroll
       for (int j = 0; j < TPT; ++j) {
-        const int u = u0 + j * kPrologueThreads + tid;
-        if (u < ns) {
-          uint32_t key = 0u;
-          if (tt[j] >= 0) {
-            key = score_key(score_pieces<R>(pc[j], qh) * sc[j]);
-            ++valid;
-          }
-          skeys[u] = key;
-        }
+        const int u = (r * TPT + j) * kPrologueThreads + tid;
+        if (u < ns) skeys[u] = sph[u] >= 0 ? score_key(score_pieces<R>(pc[j], qh) * sc[j]) : 0u;
       }
     }
-    uint32_t nvalid;
-    (void)block_excl_scan<kPrologueThreads>(valid, tmp, &nvalid);
+    // sampled pages are full pages except when every page is sampled (then
+    // the last one holds N - (n_pages - 1) P tokens)
+    const uint32_t nvalid = sp == n_pages ? (uint32_t)N : (uint32_t)ns;
     const int64_t target = (int64_t)(2 * a.B < kCandCap / 2 ? 2 * a.B : kCandCap / 2);
     int64_t ks = (nvalid * target + N - 1) / N;
     if (ks < 1) ks = 1;
     if (ks > (int64_t)nvalid) ks = nvalid;
     uint32_t kth, need;
-    block_radix_select<kPrologueThreads>(skeys, ns, (uint32_t)ks, hist, tmp, &kth, &need);
+    __syncthreads();                     // every sampled key is in LDS
+    // two 11-bit digits suffice for an estimate: tau = the lower edge of the
+    // 22-bit bin holding the ks-th sampled key
+    block_radix_select<kPrologueThreads>(skeys, ns, (uint32_t)ks, hist, tmp, &kth, &need, kDigitBits - 1);
     tau = kth;
   }
   if (tid == 0) a.tau[bh] = tau;
@@ -479,6 +484,7 @@ __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, in
     for (int i = tid; i < kHistWords; i += kFinishThreads) hist[i] = 0u;
     __syncthreads();
     for (int t0 = 0; t0 < N; t0 += kFinishThreads) {
+      asm volatile("" ::: "memory");   // qh is re-read from LDS, not held in registers
       const int t = t0 + tid;
       if (t < N) {
         const uint32_t key = token_key<R>(a, b, h, t, qh);
@@ -498,6 +504,7 @@ __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, in
   const uint32_t kth = prefix, need = k;
   uint32_t gt_run = 0, eq_run = 0;
   for (int t0 = 0; t0 < N; t0 += kFinishThreads) {
+    asm volatile("" ::: "memory");
     const int t = t0 + tid;
     const uint32_t key = t < N ? token_key<R>(a, b, h, t, qh) : 0u;
     const uint32_t gt = key > kth ? 1u : 0u, eq = (t < N && key == kth) ? 1u : 0u;
@@ -535,10 +542,21 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   const int n_chunks = (n_pages + a.cp - 1) / a.cp;
   // chunk offsets in chunk (= position) order
   const int32_t* cnts = a.chunk_cnt + bh * a.max_chunks;
+  const int cap_chunk = a.cp * a.P;
+  // the count of chunk tid and the first 16 entries of its region (a region
+  // holds at least 64) are requested together, before the count scan
+  const bool pact = !a.force_exact && tid < n_chunks;
+  const uint32_t cnt0 = pact ? (uint32_t)cnts[tid] : 0u;
+  uint4 pre[8];
+  if (pact) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.cand + (bh * a.max_chunks + tid) * (int64_t)cap_chunk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pre[j] = src[j];
+  }
   uint32_t carry = 0;
   for (int c0 = 0; c0 < n_chunks && !a.force_exact; c0 += kFinishThreads) {
     const int c = c0 + tid;
-    const uint32_t cnt = c < n_chunks ? (uint32_t)cnts[c] : 0u;
+    const uint32_t cnt = c0 == 0 ? cnt0 : (c < n_chunks ? (uint32_t)cnts[c] : 0u);
     uint32_t tot;
     const uint32_t ex = block_excl_scan<kFinishThreads>(cnt, tmp, &tot);
     if (c < n_chunks) coff[c] = carry + ex;
@@ -557,16 +575,20 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   __syncthreads();
   // gather the candidates in position order: thread c copies chunk c's
   // contiguous run to its offset; the first 16 entries are read
-  // unconditionally (a region holds at least 128), the rest, if any, one by one
+  // unconditionally (prefetched for c = tid), the rest, if any, one by one
   {
-    const int cap_chunk = a.cp * a.P;
     for (int c = tid; c < n_chunks; c += kFinishThreads) {
       const int cnt = (int)(coff[c + 1] - coff[c]);
       const uint2* src = a.cand + (bh * a.max_chunks + c) * (int64_t)cap_chunk;
       const uint32_t dst = coff[c];
       uint4 v[8];
+      if (c == tid) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const uint4*>(src)[j];
+        for (int j = 0; j < 8; ++j) v[j] = pre[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const uint4*>(src)[j];
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (2 * j < cnt) {
