@@ -48,6 +48,8 @@ constexpr int kTile = 64;                  // selected rows per tile
 constexpr int kRow = kD + 8;               // LDS row stride of K rows and Q rows (elements)
 constexpr int kPRow = kTile + 8;           // LDS row stride of P (elements)
 constexpr int kThreads = 256;
+constexpr int kChunkRows = 1024;           // rows resolved at a time (16 tiles)
+constexpr int kTilesPerChunk = kChunkRows / kTile;
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -71,9 +73,9 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   __shared__ __align__(16) uint16_t Kt[kTile * kRow];
   __shared__ __align__(16) uint16_t Qs[kHB * kRow];
   __shared__ __align__(16) uint16_t Ps[kHB * kPRow];
-  __shared__ float red_m[4][kHB];
-  __shared__ float red_l[4][kHB];
-  __shared__ int rows[3][kTile];
+  __shared__ __align__(16) float red_m[kHB][4];   // [head][wavefront]
+  __shared__ __align__(16) float red_l[kHB][4];
+  __shared__ int rows[kChunkRows];                // physical rows of the current chunk of tiles
 
   const int HB = a.Hq / kHB;
   const int L = (int)blockIdx.x;
@@ -97,39 +99,51 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   const int32_t* idx = DENSE ? nullptr : a.indices + (int64_t)b * a.B;    // Hkv = 1
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  // physical rows of tile k (-1: none) into rows[buf]; threads 0..63
-  auto fill_rows = [&](int k, int buf) {
-    if (tid < kTile) {
-      const int ii = i0 + k * kTile + tid;
-      int r = -1;
-      if (ii < i1) {
-        const int t = DENSE ? lo + ii : idx[ii];
-        if (t >= 0) r = bt[t / a.P] * a.P + (t % a.P);
-      }
-      rows[buf][tid] = r;
+  // physical rows (-1: none) of the chunk of tiles ch into rows[]: every
+  // thread resolves 4 positions, index and block-table loads batched
+  auto fill_chunk = [&](int ch) {
+    const int base = i0 + ch * kChunkRows;
+    int tv[kChunkRows / kThreads], pv[kChunkRows / kThreads];
+#pragma unroll
+    for (int j = 0; j < kChunkRows / kThreads; ++j) {
+      const int ii = base + tid + j * kThreads;
+      tv[j] = ii < i1 ? (DENSE ? lo + ii : idx[ii]) : -1;
     }
+#pragma unroll
+    for (int j = 0; j < kChunkRows / kThreads; ++j) pv[j] = tv[j] >= 0 ? bt[tv[j] / a.P] : 0;
+#pragma unroll
+    for (int j = 0; j < kChunkRows / kThreads; ++j)
+      rows[tid + j * kThreads] = tv[j] >= 0 ? pv[j] * a.P + tv[j] % a.P : -1;
   };
   // the tile's 64 x 72 16-byte pieces: 18 per thread, all loads in flight together
   constexpr int kPieces = kTile * (kD / 8) / kThreads;   // 18
-  auto fetch = [&](int buf, uint4 (&reg)[kPieces]) {
+  // (row indices read first, loads unconditional at row max(r, 0); pieces of
+  // missing rows are zeroed when stored, from the bit mask `miss`; `vld`
+  // records whether this lane's row w*16 + c of the tile exists)
+  auto fetch = [&](int kt, uint4 (&reg)[kPieces], uint32_t& miss, bool& vld) {
+    const int* rw = rows + (kt % kTilesPerChunk) * kTile;
+    int rr[kPieces];
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) rr[k] = rw[(tid + k * kThreads) / (kD / 8)];
+    vld = rw[w * 16 + c] >= 0;
+    miss = 0u;
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
-      const int q = tid + k * kThreads, tt = q / (kD / 8), cc = q % (kD / 8);
-      const int r = rows[buf][tt];
-      reg[k] = r >= 0 ? *reinterpret_cast<const uint4*>(a.k_cache + (int64_t)r * kD + cc * 8) : make_uint4(0, 0, 0, 0);
+      const int cc = (tid + k * kThreads) % (kD / 8);
+      miss |= (rr[k] < 0 ? 1u : 0u) << k;
+      reg[k] = *reinterpret_cast<const uint4*>(a.k_cache + (int64_t)(rr[k] < 0 ? 0 : rr[k]) * kD + cc * 8);
     }
   };
-  auto put = [&](const uint4 (&reg)[kPieces]) {
+  auto put = [&](const uint4 (&reg)[kPieces], uint32_t miss) {
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
       const int q = tid + k * kThreads, tt = q / (kD / 8), cc = q % (kD / 8);
-      *reinterpret_cast<uint4*>(&Kt[tt * kRow + cc * 8]) = reg[k];
+      *reinterpret_cast<uint4*>(&Kt[tt * kRow + cc * 8]) = ((miss >> k) & 1u) ? make_uint4(0, 0, 0, 0) : reg[k];
     }
   };
 
-  fill_rows(0, 0);
-  fill_rows(1, 1);
-  // Q of the 32 heads into LDS (9 pieces per thread, loads together)
+  // Q of the 32 heads into LDS (9 pieces per thread, loads together, in
+  // flight while the first chunk's rows are resolved)
   {
     constexpr int kQ = kHB * (kD / 8) / kThreads;        // 9
     uint4 qv[kQ];
@@ -138,6 +152,7 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
       const int q = tid + k * kThreads, m = q / (kD / 8), cc = q % (kD / 8);
       qv[k] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + hb * kHB + m) * kD + cc * 8);
     }
+    fill_chunk(0);
 #pragma unroll
     for (int k = 0; k < kQ; ++k) {
       const int q = tid + k * kThreads, m = q / (kD / 8), cc = q % (kD / 8);
@@ -146,7 +161,9 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   }
   __syncthreads();
   uint4 reg[kPieces];
-  fetch(0, reg);
+  uint32_t miss;
+  bool vnext;
+  fetch(0, reg, miss, vnext);
 
   // lane state: heads mt*16 + 4g + j (mt = 0, 1; j = 0..3)
   float m_run[2][4], l_run[2][4];
@@ -163,25 +180,31 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   }
 
   for (int k = 0; k < n_tiles; ++k) {
-    __syncthreads();                                   // previous tile consumed; rows[(k+1)%3] written
-    put(reg);
-    if (k + 2 < n_tiles) fill_rows(k + 2, (k + 2) % 3);
+    __syncthreads();                                   // previous tile consumed
+    put(reg, miss);
+    const bool valid = vnext;
+    if (k + 1 < n_tiles && (k + 1) % kTilesPerChunk == 0) fill_chunk((k + 1) / kTilesPerChunk);
     __syncthreads();
-    if (k + 1 < n_tiles) fetch((k + 1) % 3, reg);      // next tile's loads overlap this tile's math
-    const int* trow = rows[k % 3];
+    if (k + 1 < n_tiles) fetch(k + 1, reg, miss, vnext);     // next tile's loads overlap this tile's math
 
     // ---- S = Q K^T for rows [16w, 16w + 16)
     f32x4 S[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll 6
-    for (int ks = 0; ks < kD / 32; ++ks) {
-      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&Kt[(w * 16 + c) * kRow + ks * 32 + g * 8]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qs[(mt * 16 + c) * kRow + ks * 32 + g * 8]);
-        S[mt] = mfma16(aq, bk, S[mt]);
+    for (int k0 = 0; k0 < kD / 32; k0 += 6) {        // operands of 6 K-steps read together
+      bf16x8 bk[6], aq[2][6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int kc = (k0 + i) * 32 + g * 8;
+        bk[i] = *reinterpret_cast<const bf16x8*>(&Kt[(w * 16 + c) * kRow + kc]);
+        aq[0][i] = *reinterpret_cast<const bf16x8*>(&Qs[c * kRow + kc]);
+        aq[1][i] = *reinterpret_cast<const bf16x8*>(&Qs[(16 + c) * kRow + kc]);
+      }
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        S[0] = mfma16(aq[0][i], bk[i], S[0]);
+        S[1] = mfma16(aq[1][i], bk[i], S[1]);
       }
     }
-    const bool valid = trow[w * 16 + c] >= 0;
     float x[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -189,23 +212,28 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
       for (int j = 0; j < 4; ++j) {
         x[mt][j] = valid ? S[mt][j] * a.sm_log2 : -INFINITY;
         const float tm = row16_max(x[mt][j]);
-        if (c == 0) red_m[w][mt * 16 + g * 4 + j] = tm;
+        if (c == 0) red_m[mt * 16 + g * 4 + j][w] = tm;
       }
     __syncthreads();
     // ---- softmax update (every wavefront computes the same state)
     const int kpos = k_of_row(w * 16 + c);
+    float4 rm[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rm[mt][j] = *reinterpret_cast<const float4*>(red_m[mt * 16 + g * 4 + j]);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int hh = mt * 16 + g * 4 + j;
-        const float tm = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
+        const float tm = fmaxf(fmaxf(rm[mt][j].x, rm[mt][j].y), fmaxf(rm[mt][j].z, rm[mt][j].w));
         const float mn = fmaxf(m_run[mt][j], tm);
         const float ms = (mn == -INFINITY) ? 0.0f : mn;
         const float al = __builtin_amdgcn_exp2f(m_run[mt][j] - ms);
         const float p = __builtin_amdgcn_exp2f(x[mt][j] - ms);
         const float ps = row16_sum(p);
-        if (c == 0) red_l[w][hh] = ps;
+        if (c == 0) red_l[hh][w] = ps;
         l_run[mt][j] *= al;
         m_run[mt][j] = mn;
 #pragma unroll
@@ -217,8 +245,8 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int hh = mt * 16 + g * 4 + j;
-        l_run[mt][j] += (red_l[0][hh] + red_l[1][hh]) + (red_l[2][hh] + red_l[3][hh]);
+        const float4 rl = *reinterpret_cast<const float4*>(red_l[mt * 16 + g * 4 + j]);
+        l_run[mt][j] += (rl.x + rl.y) + (rl.z + rl.w);
       }
 
     // ---- O += P V for output dims [128w, 128w + 128)
