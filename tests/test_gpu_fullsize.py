@@ -1,0 +1,206 @@
+"""Parity at the benchmark workloads' full sizes, in the launch configuration bench.py times.
+
+Each case builds the whole workload on the GPU (synthetic generator), stores every
+cached position with jssa_store, runs one jssa_decode step (which stores the new
+token again) and the dense jssa_full_decode baseline through the C ABI with the
+workload's own shape (so the same split and chunk plans), then checks sampled
+(sequence, KV head) pairs against the oracle, each pair in full:
+
+* store: the GPU codes and scales of every position of the pair against the
+  oracle's (code distance <= 1, <= 0.1 % of codes differ; scales <= 1e-5 relative);
+* select: the GPU's top-B set against the oracle's top-B on the GPU's own codes
+  (equal sizes; differences only within 1e-5 |tau| of the B-th score);
+* attend / dense: the pair's query heads against fp64 attention over the GPU's set
+  and over all positions (or the window).
+
+The basis M is the oracle's own calibration of the layer (an input to both sides).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_decode_amd as L
+from oracle import calibrate as ocal
+from oracle import gqa as ogqa
+from oracle import mla as omla
+from synth import WORKLOADS, bf16_bits, make_gqa_calibration, make_gqa_case, make_mla_calibration, make_mla_case
+from util import check_attention, check_codes, check_selection
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@functools.lru_cache(maxsize=None)
+def _gqa_basis(name, layer):
+    w = WORKLOADS[name]
+    q, k = make_gqa_calibration(w, layer)
+    return ocal.calibrate(ocal.bf16_to_f64(bf16_bits(q)), ocal.bf16_to_f64(bf16_bits(k)), w.group,
+                          w.rank).astype(np.float32)
+
+
+@functools.lru_cache(maxsize=None)
+def _mla_basis(name):
+    w = WORKLOADS[name]
+    chunks = ((ocal.bf16_to_f64(bf16_bits(q)), ocal.bf16_to_f64(bf16_bits(l)))
+              for q, l in make_mla_calibration(w, chunk=1024))
+    return omla.calibrate(chunks, w.latent_dim, w.rank)[0].astype(np.float32)
+
+
+def _bulk_store(w, shape, flat, bt, sl, M, kp, ks):
+    P = w.page_size
+    btl = bt.long()
+    for b in range(w.batch):
+        n = int(sl[b])
+        for t0 in range(0, n, 1 << 17):
+            t = torch.arange(t0, min(n, t0 + (1 << 17)), device=DEV)
+            slots = (btl[b, t // P] * P + t % P).to(torch.int32)
+            L.jssa_store(shape, flat[slots.long()].contiguous(), slots, M, kp, ks, check_slots=False)
+
+
+def _logical(cache, bt_row, n, P):
+    """Rows of positions 0..n-1 of one sequence from a paged cache [pages, P, ...] (on the GPU)."""
+    t = torch.arange(n, device=cache.device)
+    return cache[bt_row.long()[t // P], t % P]
+
+
+def _pair_codes(kp, ks, bt_row, n, P, h):
+    """GPU codes [n, S] and scales [n] of KV head h of one sequence from the piece-major scoring cache."""
+    npg = -(-n // P)
+    pages = bt_row.long()[:npg]
+    c = kp[pages, h]                                  # [npg, S/16, P, 16]
+    c = c.permute(0, 2, 1, 3).reshape(npg * P, -1)[:n]
+    s = ks[pages, h].reshape(-1)[:n]
+    return c.cpu().numpy(), s.cpu().numpy()
+
+
+def _run_gqa(name, layer, window_layer):
+    w = WORKLOADS[name]
+    shape = L.shape_for(w)
+    case = make_gqa_case(w, device=DEV, layers=[layer])
+    lay = case.layers[layer]
+    bt, sl = case.block_table, case.seq_lens
+    out_f = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    lse_f = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    ws = L.alloc_workspace(shape)
+    window = w.window if window_layer else 0
+    L.jssa_full_decode(shape, lay.q, lay.k_cache, lay.v_cache, bt, sl, window, w.sm_scale, out_f, ws, lse_f)
+    res = dict(w=w, case=case, lay=lay, out_f=out_f.float().cpu().numpy(), lse_f=lse_f.cpu().numpy())
+    if window_layer:
+        return res
+    m32 = _gqa_basis(name, layer)
+    M = torch.from_numpy(m32).to(DEV)
+    kp, ks = L.alloc_scoring_cache(shape, lay.k_cache.shape[0], DEV)
+    flat = lay.k_cache.view(-1, w.num_kv_heads, w.head_dim)
+    _bulk_store(w, shape, flat, bt, sl, M, kp, ks)
+    P = w.page_size
+    last = sl.long() - 1
+    slot_new = (bt.long()[torch.arange(w.batch, device=DEV), last // P] * P + last % P).to(torch.int32)
+    k_new = flat[slot_new.long()].contiguous()
+    idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=DEV)
+    out = torch.empty_like(out_f)
+    lse = torch.empty_like(lse_f)
+    L.jssa_decode(shape, lay.q, k_new, slot_new, M, kp, ks, lay.k_cache, lay.v_cache, bt, sl, idx, w.sm_scale, out,
+                  ws, lse)
+    torch.cuda.synchronize()
+    res.update(m32=m32, kp=kp, ks=ks, idx=idx.cpu().numpy(), out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+    return res
+
+
+def _pairs(w):
+    return [(0, 0), (w.batch // 2, w.num_kv_heads - 1), (w.batch - 1, w.num_kv_heads // 2)]
+
+
+@pytest.mark.parametrize("name,layer", [("llama8b_128k", 0), ("llama8b_32k", 0), ("hybrid_64k", 1)])
+def test_fullsize_gqa_decode_step(name, layer):
+    r = _run_gqa(name, layer, window_layer=False)
+    w, case, lay = r["w"], r["case"], r["lay"]
+    q = bf16_bits(lay.q)
+    G, P = w.group, w.page_size
+    for b, h in _pairs(w):
+        n = int(case.seq_lens[b])
+        rk = bf16_bits(_logical(lay.k_cache, case.block_table[b], n, P)[:, h])
+        rv = bf16_bits(_logical(lay.v_cache, case.block_table[b], n, P)[:, h])
+        codes, scale = _pair_codes(r["kp"], r["ks"], case.block_table[b], n, P, h)
+        oc, os_ = ogqa.store(rk[:, None, :], r["m32"][h:h + 1])
+        check_codes(codes, oc[:, 0])
+        assert np.all(np.abs(scale.astype(np.float64) - os_[:, 0]) <= 1e-5 * np.abs(os_[:, 0]))
+        qhat = ogqa.project_query(q[b], r["m32"], G)[h]
+        sc = ogqa.scores(qhat, codes, scale)
+        oidx, tau = ogqa.select_topb(sc, w.budget)
+        check_selection(r["idx"][b, h], oidx, sc, tau)
+        for g in range(G):
+            j = h * G + g
+            sel = r["idx"][b, h][r["idx"][b, h] >= 0]
+            o, l = ogqa.attend(q[b, j], rk[sel], rv[sel], w.sm_scale)
+            check_attention(r["out"][b, j], o)
+            assert abs(r["lse"][b, j] - l) <= 1e-3
+            o, l = ogqa.attend(q[b, j], rk, rv, w.sm_scale)
+            check_attention(r["out_f"][b, j], o)
+            assert abs(r["lse_f"][b, j] - l) <= 1e-3
+    del r
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_hybrid_window_layer():
+    r = _run_gqa("hybrid_64k", 0, window_layer=True)
+    w, case, lay = r["w"], r["case"], r["lay"]
+    q = bf16_bits(lay.q)
+    for b, h in _pairs(w):
+        n = int(case.seq_lens[b])
+        rk = bf16_bits(_logical(lay.k_cache, case.block_table[b], n, w.page_size)[:, h])
+        rv = bf16_bits(_logical(lay.v_cache, case.block_table[b], n, w.page_size)[:, h])
+        sel = ogqa.window_indices(n, w.window)
+        for g in range(w.group):
+            j = h * w.group + g
+            o, l = ogqa.attend(q[b, j], rk[sel], rv[sel], w.sm_scale)
+            check_attention(r["out_f"][b, j], o)
+            assert abs(r["lse_f"][b, j] - l) <= 1e-3
+    del r
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_mla_decode_step():
+    name = "mla_128k"
+    w = WORKLOADS[name]
+    shape = L.shape_for(w)
+    case = make_mla_case(w, device=DEV)
+    bt, sl, P = case.block_table, case.seq_lens, w.page_size
+    m32 = _mla_basis(name)
+    M = torch.from_numpy(m32).to(DEV)
+    kp, ks = L.alloc_scoring_cache(shape, case.latent.shape[0], DEV)
+    flat = case.latent.view(-1, w.head_dim)
+    _bulk_store(w, shape, flat, bt, sl, M, kp, ks)
+    last = sl.long() - 1
+    slot_new = (bt.long()[torch.arange(w.batch, device=DEV), last // P] * P + last % P).to(torch.int32)
+    k_new = flat[slot_new.long()].contiguous()
+    ws = L.alloc_workspace(shape)
+    idx = torch.empty((w.batch, 1, w.budget), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    out_f, lse_f = torch.empty_like(out), torch.empty_like(lse)
+    L.jssa_decode(shape, case.q, k_new, slot_new, M, kp, ks, case.latent, None, bt, sl, idx, w.sm_scale, out, ws, lse)
+    L.jssa_full_decode(shape, case.q, case.latent, None, bt, sl, 0, w.sm_scale, out_f, ws, lse_f)
+    torch.cuda.synchronize()
+    gidx, got, glse = idx.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy()
+    gotf, glsef = out_f.float().cpu().numpy(), lse_f.cpu().numpy()
+    q = bf16_bits(case.q)
+    for b in (0, w.batch - 1):
+        n = int(sl[b])
+        rows = bf16_bits(_logical(case.latent, bt[b], n, P))
+        codes, scale = _pair_codes(kp, ks, bt[b], n, P, 0)
+        oc, os_ = omla.store(rows, m32)
+        check_codes(codes, oc)
+        assert np.all(np.abs(scale.astype(np.float64) - os_) <= 1e-5 * np.abs(os_))
+        qhat = omla.project_query(q[b], m32)
+        sc = ogqa.scores(qhat, codes, scale)
+        oidx, tau = ogqa.select_topb(sc, w.budget)
+        check_selection(gidx[b, 0], oidx, sc, tau)
+        o, l = omla.attend(q[b], rows[gidx[b, 0][gidx[b, 0] >= 0]], w.sm_scale)
+        check_attention(got[b], o)
+        assert np.all(np.abs(glse[b] - l) <= 1e-3)
+        o, l = omla.attend(q[b], rows, w.sm_scale)
+        check_attention(gotf[b], o)
+        assert np.all(np.abs(glsef[b] - l) <= 1e-3)
+    torch.cuda.empty_cache()
