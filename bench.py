@@ -514,6 +514,9 @@ def main():
         "select_finish": sel(L.STAGE_FINISH),
         "attend": lambda r: L.jssa_attend(shape, lay_of(r).q, lay_of(r).kc, lay_of(r).vc, bt, sl, idx, w.sm_scale,
                                           out, ws),
+        # the gather-then-attend baseline over the same selection (staging copy + dense attention)
+        "gather_attend": lambda r: L.jssa_gather_attend(shape, lay_of(r).q, lay_of(r).kc, lay_of(r).vc, bt, sl, idx,
+                                                        w.sm_scale, out, ws),
     }
     win = [(r, i) for r in range(n_rep) for i, lay in enumerate(reps[r]) if lay.window]
     if win:
@@ -590,6 +593,9 @@ def main():
         "full_kv_gbps": round(full_bytes / (ms_full * 1e-3) / 1e9, 1),
         "speedup_vs_full_kv": round(ms_full / ms, 3),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "gather_free_vs_gather": {
+            "attend_ms": round(stage_ms["attend"], 5), "gather_then_attend_ms": round(stage_ms["gather_attend"], 5),
+            "ratio": round(stage_ms["gather_attend"] / stage_ms["attend"], 3)},
         "host_wall_ms_per_step": round(wall_ms, 5),
         **extra,
         "context": "pages' own figure: up to 6.43x end-to-end over full KV at 128K on one NVIDIA B200 "

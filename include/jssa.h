@@ -177,6 +177,23 @@ int32_t jssa_full_decode(const jssa_shape* shape, const uint16_t* q, const uint1
                          int32_t window, float sm_scale, uint16_t* out, float* lse_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* jssa_gather_attend — the gather-then-attend baseline that gather-free indexed
+ * attention replaces (summary page §3.3 and "Ablation Studies", Figure 6;
+ * README page "4. vLLM configuration reference": indexed attention off).  Same
+ * arguments and result as jssa_attend: the selected K/V rows of every (sequence,
+ * KV head) are first copied into a staging cache inside the workspace (slot i of
+ * head h holds that head's i-th selected position, with an identity block
+ * table), then the dense attention of jssa_full_decode runs over the first
+ * min(N, B) staged slots.  indices must be as jssa_select writes them (the -1
+ * entries only as trailing padding); a -1 inside the first min(N, B) entries is
+ * staged as a zero row and takes part in the softmax.  The workspace from
+ * jssa_workspace_bytes includes the staging cache (batch * ceil(B/page) * page
+ * rows of K and V per KV head). */
+int32_t jssa_gather_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
+                           const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* indices, float sm_scale, uint16_t* out, float* lse_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* jssa_calib_moments — calibration second moments (summary page §3.2; README
  * page §2): ADDS sum_t qbar_t qbar_t^T to gq and sum_t k_t k_t^T to gk (fp32,
  * [Hkv, dm, dm]; dm = d, MLA dm = 512 over the latent dims), so a long

@@ -26,7 +26,7 @@ MLA_LATENT, MLA_ROPE = 512, 64
 
 EXPORTED = ("jssa_status_string", "jssa_workspace_bytes", "jssa_kp_page_bytes", "jssa_store", "jssa_select",
             "jssa_select_stages",
-            "jssa_attend", "jssa_decode", "jssa_full_decode", "jssa_calib_workspace_bytes",
+            "jssa_attend", "jssa_decode", "jssa_full_decode", "jssa_gather_attend", "jssa_calib_workspace_bytes",
             "jssa_calib_moments", "jssa_basis")
 
 
@@ -70,6 +70,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "jssa_attend": (I32, [S, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]),
         "jssa_decode": (I32, [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]),
         "jssa_full_decode": (I32, [S, P, P, P, P, P, I32, ctypes.c_float, P, P, P, SZ, P]),
+        "jssa_gather_attend": (I32, [S, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]),
         "jssa_calib_workspace_bytes": (I32, [S, I32, ctypes.POINTER(SZ)]),
         "jssa_calib_moments": (I32, [S, P, P, I32, P, P, P, SZ, P]),
         "jssa_basis": (I32, [S, P, P, P]),
@@ -272,6 +273,22 @@ def jssa_full_decode(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cac
             _ptr("lse_out", lse_out, torch.float32, (shape.batch, shape.num_q_heads), optional=True),
             *_ws(shape, workspace))
     _check("jssa_full_decode", _lib.jssa_full_decode(ctypes.byref(shape), *args, _stream()))
+
+
+def jssa_gather_attend(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
+                       block_table: torch.Tensor, seq_lens: torch.Tensor, indices: torch.Tensor, sm_scale: float,
+                       out: torch.Tensor, workspace: torch.Tensor, lse_out: Optional[torch.Tensor] = None) -> None:
+    n, cs = _cache_shape(shape, k_cache)
+    args = (_ptr("q", q, torch.bfloat16, (shape.batch, shape.num_q_heads, shape.head_dim)),
+            _ptr("k_cache", k_cache, torch.bfloat16, cs),
+            _ptr("v_cache", v_cache, torch.bfloat16, cs, optional=shape.kind == KIND_MLA),
+            *_table_args(shape, block_table, seq_lens),
+            _ptr("indices", indices, torch.int32, (shape.batch, shape.num_kv_heads, shape.budget)),
+            ctypes.c_float(sm_scale),
+            _ptr("out", out, torch.bfloat16, (shape.batch, shape.num_q_heads, shape.v_dim)),
+            _ptr("lse_out", lse_out, torch.float32, (shape.batch, shape.num_q_heads), optional=True),
+            *_ws(shape, workspace))
+    _check("jssa_gather_attend", _lib.jssa_gather_attend(ctypes.byref(shape), *args, _stream()))
 
 
 def calib_workspace_bytes(shape: Shape, T: int) -> int:

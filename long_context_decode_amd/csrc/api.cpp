@@ -25,7 +25,9 @@ struct Plan {
   int dn_splits, dn_len;     // dense (window 0) split plan
   int ml_splits, ml_len;     // MLA sparse attention split plan
   int md_splits, md_len;     // MLA dense (window 0) split plan
-  size_t off_qhat, off_tau, off_chunk, off_cand, off_part_o, off_part_ml, total;
+  int stage_pages;            // gather-then-attend staging cache: pages per sequence
+  size_t off_qhat, off_tau, off_chunk, off_cand, off_part_o, off_part_ml;
+  size_t off_stage_k, off_stage_v, off_stage_table, off_stage_lens, total;
 };
 
 // Split plan of the attention kernels: about 512 blocks of four wavefronts,
@@ -113,7 +115,12 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
     p->ml_splits = (int)cdiv(n, p->ml_len);
     mla_dense_plan(p->maxN, p->batch, p->Hq, &p->md_splits, &p->md_len);
   }
-  const int max_splits = std::max({p->sp_splits, p->dn_splits, p->mla ? std::max(p->ml_splits, p->md_splits) : 1});
+  p->stage_pages = (int)cdiv(p->B, p->P);
+  int st_splits, st_len;                    // dense attention over the staging cache
+  if (p->mla) mla_dense_plan((int64_t)p->stage_pages * p->P, p->batch, p->Hq, &st_splits, &st_len);
+  else split_plan((int64_t)p->stage_pages * p->P, p->batch * p->Hkv, &st_splits, &st_len);
+  const int max_splits =
+      std::max({p->sp_splits, p->dn_splits, st_splits, p->mla ? std::max(p->ml_splits, p->md_splits) : 1});
   const size_t bh = (size_t)p->batch * p->Hkv;
   const size_t cand = bh * p->max_chunks * p->cp * p->P;   // one region per stream chunk
   size_t off = 0;
@@ -124,6 +131,11 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   const size_t pj = (size_t)p->batch * p->Hq * max_splits;
   p->off_part_o = off;  off = align_up(off + pj * p->dv * sizeof(float));
   p->off_part_ml = off; off = align_up(off + pj * 2 * sizeof(float));
+  const size_t stage_rows = (size_t)p->batch * p->stage_pages * p->P * p->Hkv;
+  p->off_stage_k = off; off = align_up(off + stage_rows * p->d * sizeof(uint16_t));
+  p->off_stage_v = off; off = align_up(off + (p->mla ? 0 : stage_rows * p->d * sizeof(uint16_t)));
+  p->off_stage_table = off; off = align_up(off + (size_t)p->batch * p->stage_pages * sizeof(int32_t));
+  p->off_stage_lens = off; off = align_up(off + (size_t)p->batch * sizeof(int32_t));
   p->total = off;
   return JSSA_OK;
 }
@@ -353,6 +365,45 @@ int32_t jssa_full_decode(const jssa_shape* shape, const uint16_t* q, const uint1
   if (st != JSSA_OK) return st;
   return do_attend(p, q, k_cache, v_cache, block_table, seq_lens, nullptr, window, sm_scale, out, lse_out, workspace,
                    workspace_bytes, stream);
+}
+
+int32_t jssa_gather_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
+                           const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* indices, float sm_scale, uint16_t* out, float* lse_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !indices || !out || !workspace)
+    return JSSA_ERR_NULL;
+  if (workspace_bytes < p.total) return JSSA_ERR_WORKSPACE;
+  GatherArgs g{};
+  g.k_cache = k_cache;
+  g.v_cache = p.mla ? nullptr : v_cache;
+  g.block_table = block_table;
+  g.seq_lens = seq_lens;
+  g.indices = indices;
+  g.stage_k = at<uint16_t>(workspace, p.off_stage_k);
+  g.stage_v = p.mla ? nullptr : at<uint16_t>(workspace, p.off_stage_v);
+  g.stage_table = at<int32_t>(workspace, p.off_stage_table);
+  g.stage_lens = at<int32_t>(workspace, p.off_stage_lens);
+  g.batch = p.batch;
+  g.Hkv = p.Hkv;
+  g.P = p.P;
+  g.max_pages = p.max_pages;
+  g.B = p.B;
+  g.row_elems = p.d;
+  g.stage_pages = p.stage_pages;
+  hipError_t e = launch_gather(g, stream);
+  if (e != hipSuccess) return JSSA_ERR_HIP;
+  // dense attention over the staging cache: its own page count and split plans
+  Plan ps = p;
+  ps.max_pages = p.stage_pages;
+  ps.maxN = (int64_t)p.stage_pages * p.P;
+  split_plan(ps.maxN, p.batch * p.Hkv, &ps.dn_splits, &ps.dn_len);
+  mla_dense_plan(ps.maxN, p.batch, p.Hq, &ps.md_splits, &ps.md_len);
+  return do_attend(ps, q, g.stage_k, g.stage_v, g.stage_table, g.stage_lens, nullptr, 0, sm_scale, out, lse_out,
+                   workspace, workspace_bytes, stream);
 }
 
 int32_t jssa_calib_workspace_bytes(const jssa_shape* shape, int32_t T, size_t* bytes) {

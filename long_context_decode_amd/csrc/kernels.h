@@ -61,6 +61,19 @@ struct AttendArgs {
   int splits, split_len;
 };
 
+struct GatherArgs {
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;   // NULL for MLA (one latent row)
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* indices;    // [batch, Hkv, B]
+  uint16_t* stage_k;         // staging cache [batch * stage_pages, P, Hkv, row_elems]
+  uint16_t* stage_v;
+  int32_t* stage_table;      // [batch, stage_pages] identity block table
+  int32_t* stage_lens;       // [batch] min(N, B)
+  int batch, Hkv, P, max_pages, B, row_elems, stage_pages;
+};
+
 struct CalibArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -77,6 +90,7 @@ hipError_t launch_attend(const AttendArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_mla_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttendArgs& a, int dv, hipStream_t s);
 hipError_t launch_calib(const CalibArgs& a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 
 // host: per-head top-r eigenvectors of the unit-trace-normalised moment sum
 int32_t basis_impl(int hkv, int n, int r, const float* gq, const float* gk, float* m_out);

@@ -57,9 +57,11 @@ def test_shape_validation(kw, status):
 def test_workspace_and_page_sizes():
     s = _shape()
     ws = L.workspace_bytes(s)
-    # candidate regions dominate: one (key, position) slot per cached token and KV head
+    # candidate regions (one (key, position) slot per cached token and KV head) and the
+    # gather-then-attend staging cache (B rows of K and V per sequence and KV head) dominate
     cand = 8 * 8 * 8192 * 16 * 8
-    assert cand < ws < cand + 16 * 1024 * 1024
+    stage = 2 * 8 * 8 * 2048 * 128 * 2
+    assert cand + stage < ws < cand + stage + 16 * 1024 * 1024
     assert L.kp_page_bytes(s) == (8 * 16 * 32, 8 * 16)
     m = _shape(kind=1, num_kv_heads=1, num_q_heads=128, head_dim=576, rank=64, page_size=64)
     assert L.kp_page_bytes(m) == (64 * 128, 64)
@@ -77,6 +79,8 @@ def test_entry_points_reject_before_launch():
     assert lib.jssa_attend(ref, fake, fake, fake, fake, fake, nul, 0.1, fake, nul, fake, 1 << 40, nul) == -1
     assert lib.jssa_attend(ref, fake, fake, fake, fake, fake, fake, 0.1, fake, nul, fake, 16, nul) == -4
     assert lib.jssa_full_decode(ref, fake, fake, fake, fake, fake, -1, 0.1, fake, nul, fake, 1 << 40, nul) == -2
+    assert lib.jssa_gather_attend(ref, fake, fake, fake, fake, fake, nul, 0.1, fake, nul, fake, 1 << 40, nul) == -1
+    assert lib.jssa_gather_attend(ref, fake, fake, fake, fake, fake, fake, 0.1, fake, nul, fake, 16, nul) == -4
     assert lib.jssa_decode(ref, fake, fake, nul, fake, fake, fake, fake, fake, fake, fake, fake, 0.1, fake, nul,
                            fake, 1 << 40, nul) == -1
     assert lib.jssa_store(ref, nul, fake, 4, fake, fake, fake, nul) == -1

@@ -663,3 +663,49 @@ def test_hybrid_stack_layers_in_sequence():
                 o, _ = ogqa.attend_group(q[b, j0:j0 + w.group], rows_k[b][:, h], rows_v[b][:, h], gidx[b, h],
                                          w.sm_scale)
                 check_attention(got[b, j0:j0 + w.group], o)
+
+
+# ----------------------------------------------------------------------------- gather-then-attend
+
+@pytest.mark.parametrize("name", ["mid_sampled", "d256_r48", "short_ctx", "page32_g8"])
+def test_gather_attend_parity(name):
+    """Staged (gathered) rows + dense attention give the indexed attention's result."""
+    w, case, m32, rows_k, rows_v, stored = _gqa(name)
+    shape, kp, ks, M = _upload(w, case, m32, stored)
+    lay = case.layers[0]
+    btd, sld = case.block_table.to(DEV), case.seq_lens.to(DEV)
+    ws = L.alloc_workspace(shape)
+    idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=DEV)
+    L.jssa_select(shape, lay.q.to(DEV), M, kp, ks, btd, sld, idx, ws)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    L.jssa_gather_attend(shape, lay.q.to(DEV), lay.k_cache.to(DEV), lay.v_cache.to(DEV), btd, sld, idx, w.sm_scale,
+                         out, ws, lse)
+    gidx, got, glse = idx.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy()
+    q = bf16_bits(lay.q)
+    for b in range(w.batch):
+        for h in range(w.num_kv_heads):
+            j0 = h * w.group
+            o, l = ogqa.attend_group(q[b, j0:j0 + w.group], rows_k[b][:, h], rows_v[b][:, h], gidx[b, h], w.sm_scale)
+            check_attention(got[b, j0:j0 + w.group], o)
+            assert np.all(np.abs(glse[b, j0:j0 + w.group] - l) <= 1e-3)
+
+
+def test_gather_attend_parity_mla():
+    w, case, m32, rows, stored = _mla("mla_sampled")
+    q = bf16_bits(case.q)
+    idx = np.full((w.batch, 1, w.budget), -1, np.int32)
+    for b in range(w.batch):
+        s = ogqa.scores(omla.project_query(q[b], m32), stored[b][0], stored[b][1])
+        idx[b, 0], _ = ogqa.select_topb(s, w.budget)
+    shape = L.shape_for(w)
+    out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    L.jssa_gather_attend(shape, case.q.to(DEV), case.latent.to(DEV), None, case.block_table.to(DEV),
+                         case.seq_lens.to(DEV), torch.from_numpy(idx).to(DEV), w.sm_scale, out,
+                         L.alloc_workspace(shape), lse)
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(w.batch):
+        o, l = omla.attend(q[b], rows[b][idx[b, 0][idx[b, 0] >= 0]], w.sm_scale)
+        check_attention(got[b], o)
+        assert np.all(np.abs(glse[b] - l) <= 1e-3)
