@@ -15,6 +15,10 @@ Step by step, in the order of the paper summary page, §3.1 Overview, in fp64:
 Readings where the pages are silent (each listed in the design doc):
   * scale = fp32(max_i |y_i| / 448); codes = RNE-saturating E4M3FN of y_i/scale
     (a zero row stores scale 0 and zero codes);
+  * scoring-cache variants (README §4 "Notes": r bytes per token and KV head):
+    "e8m0" stores the scale as one byte E with value 2^(E-127), E - 127 =
+    ceil(log2 of the fp32 scale above), codes of y_i / 2^(E-127); "none"
+    stores no scale, codes of y_i themselves (saturating);
   * the score is scale * sum_i qhat_i dec(code_i) and -0 counts as +0;
   * order by (score descending, position ascending): on a tie at the B-th score
     the lowest position wins; output positions ascending, padded with -1;
@@ -42,26 +46,57 @@ def logical_rows(cache: np.ndarray, block_row: np.ndarray, n: int, page: int) ->
 
 # ------------------------------------------------------------------ store
 
-def store(k_u16: np.ndarray, m32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+def store(k_u16: np.ndarray, m32: np.ndarray, fmt: str = "fp32") -> Tuple[np.ndarray, np.ndarray]:
     """Project and FP8-quantise keys.
 
     k_u16 [T, Hkv, d] bf16 bits; m32 [Hkv, r, d] float32 basis.
-    Returns codes uint8 [T, Hkv, r] and scales float32 [T, Hkv]."""
+    Returns codes uint8 [T, Hkv, r] and stored scales [T, Hkv] (see quantise_rows)."""
     k = bf16_to_f64(k_u16)
     m = np.asarray(m32, dtype=np.float32).astype(np.float64)
     y = np.einsum("hrd,thd->thr", m, k)
-    return quantise_rows(y)
+    return quantise_rows(y, fmt)
 
 
-def quantise_rows(y: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Per-row (last axis) absmax scaling to the E4M3FN range."""
+SCALE_FORMATS = ("fp32", "e8m0", "none")
+
+
+def e8m0_decode(b: np.ndarray) -> np.ndarray:
+    """OCP microscaling E8M0 scale byte -> 2^(E - 127) (E = 255, NaN, is never stored)."""
+    return np.ldexp(1.0, np.asarray(b).astype(np.int64) - 127)
+
+
+def quantise_rows(y: np.ndarray, fmt: str = "fp32") -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row (last axis) absmax scaling to the E4M3FN range.
+
+    Returns (codes uint8 [..., S], stored scales): float32 for "fp32", uint8
+    E8M0 bytes for "e8m0", None for "none"."""
+    if fmt == "none":
+        return fp8.encode(y), None
     a = np.max(np.abs(y), axis=-1)
     scale = (a / fp8.MAX_FINITE).astype(np.float32)
     s64 = scale.astype(np.float64)
+    if fmt == "e8m0":
+        m, e = np.frexp(s64)                          # s = m 2^e, m in [0.5, 1): ceil(log2 s) = e, or e - 1 at m = 0.5
+        e = np.clip(np.where(m == 0.5, e - 1, e), -127, 127)
+        stored = np.where(s64 > 0, e + 127, 0).astype(np.uint8)
+        s64 = np.where(s64 > 0, np.ldexp(1.0, e), 0.0)
+    elif fmt != "fp32":
+        raise ValueError(fmt)
+    else:
+        stored = scale
     safe = np.where(s64 > 0, s64, 1.0)
     codes = fp8.encode(y / safe[..., None])
     codes = np.where((s64 > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
-    return codes, scale
+    return codes, stored
+
+
+def scale_multiplier(stored, fmt: str = "fp32"):
+    """Stored scales -> the factor the score is multiplied by (fp64)."""
+    if fmt == "none":
+        return 1.0
+    if fmt == "e8m0":
+        return e8m0_decode(stored)
+    return np.asarray(stored, dtype=np.float32).astype(np.float64)
 
 
 # ------------------------------------------------------------------ project + score
@@ -73,9 +108,9 @@ def project_query(q_u16: np.ndarray, m32: np.ndarray, group: int) -> np.ndarray:
     return np.einsum("hrd,hd->hr", m, qbar)
 
 
-def scores(qhat: np.ndarray, codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """Projected scores of one KV head: qhat [r], codes [N, r], scale [N] -> [N] fp64."""
-    s = np.asarray(scale, dtype=np.float32).astype(np.float64) * (fp8.decode(codes) @ qhat)
+def scores(qhat: np.ndarray, codes: np.ndarray, scale, fmt: str = "fp32") -> np.ndarray:
+    """Projected scores of one KV head: qhat [r], codes [N, r], stored scales [N] -> [N] fp64."""
+    s = scale_multiplier(scale, fmt) * (fp8.decode(codes) @ qhat)
     return np.where(s == 0.0, 0.0, s)
 
 
@@ -136,7 +171,7 @@ def window_indices(n: int, window: int) -> np.ndarray:
 # ------------------------------------------------------------------ one full step
 
 def decode_step(q_u16: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, m32: np.ndarray,
-                budget: int, sm: float, codes: np.ndarray = None, scale: np.ndarray = None):
+                budget: int, sm: float, codes: np.ndarray = None, scale: np.ndarray = None, fmt: str = "fp32"):
     """One sequence, all KV heads: store all keys (unless codes/scale given), select, attend.
 
     q_u16 [Hq, d]; k_rows, v_rows [N, Hkv, d]; m32 [Hkv, r, d].
@@ -144,7 +179,7 @@ def decode_step(q_u16: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, m32: 
     hkv = k_rows.shape[1]
     group = q_u16.shape[0] // hkv
     if codes is None:
-        codes, scale = store(k_rows, m32)
+        codes, scale = store(k_rows, m32, fmt)
     qhat = project_query(q_u16, m32, group)
     n = k_rows.shape[0]
     sc = np.zeros((hkv, n))
@@ -153,7 +188,7 @@ def decode_step(q_u16: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, m32: 
     out = np.zeros((q_u16.shape[0], v_rows.shape[2]))
     lse = np.zeros(q_u16.shape[0])
     for h in range(hkv):
-        sc[h] = scores(qhat[h], codes[:, h], scale[:, h])
+        sc[h] = scores(qhat[h], codes[:, h], None if scale is None else scale[:, h], fmt)
         idx[h], tau[h] = select_topb(sc[h], budget)
         o, l = attend_group(q_u16[h * group:(h + 1) * group], k_rows[:, h], v_rows[:, h], idx[h], sm)
         out[h * group:(h + 1) * group] = o

@@ -31,9 +31,9 @@ def scoring_rows(rows64: np.ndarray, m32: np.ndarray, latent: int) -> np.ndarray
     return np.concatenate([rows64[:, :latent] @ m.T, rows64[:, latent:]], axis=1)
 
 
-def store(rows_u16: np.ndarray, m32: np.ndarray, latent: int = 512) -> Tuple[np.ndarray, np.ndarray]:
-    """rows [T, 576] bf16 bits -> codes uint8 [T, r+rope], scale float32 [T]."""
-    return quantise_rows(scoring_rows(bf16_to_f64(rows_u16), m32, latent))
+def store(rows_u16: np.ndarray, m32: np.ndarray, latent: int = 512, fmt: str = "fp32") -> Tuple[np.ndarray, np.ndarray]:
+    """rows [T, 576] bf16 bits -> codes uint8 [T, r+rope], stored scales [T] (see gqa.quantise_rows)."""
+    return quantise_rows(scoring_rows(bf16_to_f64(rows_u16), m32, latent), fmt)
 
 
 def project_query(q_u16: np.ndarray, m32: np.ndarray, latent: int = 512) -> np.ndarray:

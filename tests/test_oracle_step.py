@@ -308,3 +308,70 @@ def test_mla_attend_matches_sdpa_and_needles_selected():
         torch.as_tensor(cal.bf16_to_f64(q))[None, :, None], kv[None, None], kv[None, None, :, :512],
         scale=w.sm_scale)[0, :, 0].numpy()
     assert np.abs(res["out"] - ref).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------- scoring-cache scale formats
+
+def test_e8m0_decode_matches_the_microscaling_definition():
+    """E8M0 value 2^(E - 127): E = 127 is 1, 0 is 2^-127, 254 is 2^127 (OCP microscaling formats spec)."""
+    assert gqa.e8m0_decode(np.array([127]))[0] == 1.0
+    assert gqa.e8m0_decode(np.array([0]))[0] == 2.0 ** -127
+    assert gqa.e8m0_decode(np.array([254]))[0] == 2.0 ** 127
+    assert gqa.e8m0_decode(np.array([130]))[0] == 8.0
+
+
+def test_e8m0_scale_is_the_smallest_power_of_two_keeping_rows_in_range():
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((4000, 32)) * np.exp(rng.uniform(-20, 20, (4000, 1)))
+    y[0] = 0.0
+    codes, stored = gqa.quantise_rows(y, "e8m0")
+    mult = gqa.e8m0_decode(stored)
+    s32 = (np.abs(y).max(axis=1) / 448.0).astype(np.float32).astype(np.float64)
+    nz = s32 > 0
+    # smallest power of two >= the fp32 scale: 2^e >= s > 2^(e-1)
+    assert np.all(mult[nz] >= s32[nz]) and np.all(mult[nz] / 2 < s32[nz])
+    assert np.all(codes[0] == 0) and stored[0] == 0
+    # dividing by a power of two is exact: the codes are those of y * 2^-e
+    assert np.array_equal(codes[nz], fp8.encode(y[nz] / mult[nz, None]))
+    # the scaled rows stay in range: |y| / 2^e <= 448
+    assert np.all(np.abs(y[nz]) / mult[nz, None] <= 448.0)
+
+
+def test_e8m0_equals_fp32_when_the_scale_is_a_power_of_two():
+    y = np.zeros((3, 16))
+    y[:, 0] = [448.0 * 0.25, 448.0 * 8.0, 448.0 * 2.0 ** -20]
+    y[:, 1] = [1.0, -3.0, 2.0 ** -21]
+    c32, s32 = gqa.quantise_rows(y, "fp32")
+    c8, s8 = gqa.quantise_rows(y, "e8m0")
+    assert np.array_equal(c32, c8)
+    assert np.array_equal(s32.astype(np.float64), gqa.e8m0_decode(s8))
+    assert np.array_equal(gqa.scores(np.ones(16), c32, s32, "fp32"), gqa.scores(np.ones(16), c8, s8, "e8m0"))
+
+
+def test_unscaled_format_stores_the_projection_itself():
+    rng = np.random.default_rng(6)
+    y = rng.standard_normal((100, 32)) * 50.0
+    y[0, 0] = 1000.0                                    # beyond the E4M3FN range: saturates to 448
+    codes, stored = gqa.quantise_rows(y, "none")
+    assert stored is None
+    assert np.array_equal(codes, fp8.encode(y))
+    assert fp8.decode(codes[:1, :1])[0, 0] == 448.0
+    q = rng.standard_normal(32)
+    assert np.allclose(gqa.scores(q, codes, None, "none"), fp8.decode(codes) @ q, rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("fmt", ["e8m0", "none"])
+def test_scale_formats_keep_the_needles(fmt):
+    """Every planted needle is still selected with the coarser scoring caches."""
+    from synth import WORKLOADS, make_gqa_case, make_gqa_calibration, bf16_bits
+    w = WORKLOADS["tiny"]
+    q, k = make_gqa_calibration(w, 0)
+    m32 = cal.calibrate(cal.bf16_to_f64(bf16_bits(q)), cal.bf16_to_f64(bf16_bits(k)), w.group, w.rank).astype(np.float32)
+    case = make_gqa_case(w)
+    lay = case.layers[0]
+    bt, n = case.block_table.numpy(), int(case.seq_lens[0])
+    kr = gqa.logical_rows(bf16_bits(lay.k_cache), bt[0], n, w.page_size)
+    vr = gqa.logical_rows(bf16_bits(lay.v_cache), bt[0], n, w.page_size)
+    r = gqa.decode_step(bf16_bits(lay.q)[0], kr, vr, m32, w.budget, w.sm_scale, fmt=fmt)
+    for h in range(w.num_kv_heads):
+        assert set(lay.needles[(0, h)]) <= set(r["idx"][h])
