@@ -63,7 +63,10 @@ def _src_hash(*names):
 
 # ----------------------------------------------------------------------------- algorithmic bytes
 
-def layer_bytes(w, seq_lens, mode):
+SCALE_BYTES = {"fp32": 4, "e8m0": 1, "none": 0}
+
+
+def layer_bytes(w, seq_lens, mode, scale_format="fp32"):
     """Bytes one layer must move per step.  mode: 'sparse' (JSSA), 'full' (all positions), 'window'."""
     S, d, hkv, hq, B = w.score_dims, w.head_dim, w.num_kv_heads, w.num_q_heads, w.budget
     row = d * 2 if w.kind == "mla" else 2 * d * 2    # one latent row (K = V) / one K + V pair per KV head
@@ -73,21 +76,22 @@ def layer_bytes(w, seq_lens, mode):
     if mode == "window":      # only the window's pages of the block table are read
         io_w = w.batch * hq * (d + w.v_dim) * 2 + w.batch * (-(-w.window // w.page_size)) * 4
         return {"kv": sum(min(n, w.window) * hkv * row for n in seq_lens), "q_out_table": io_w}
-    return {"score": sum(n * hkv * (S + 4) for n in seq_lens),
+    sb = SCALE_BYTES[scale_format]
+    return {"score": sum(n * hkv * (S + sb) for n in seq_lens),
             "selected_kv": sum(min(B, n) * hkv * row for n in seq_lens),
             "indices": w.batch * hkv * B * 4 * 2,
             "q_out_table": io,
-            "store": w.batch * hkv * (d * 2 + S + 4)}
+            "store": w.batch * hkv * (d * 2 + S + sb)}
 
 
-def step_bytes(w, seq_lens, sparse=True):
+def step_bytes(w, seq_lens, sparse=True, scale_format="fp32"):
     """Sum over the step's layers, with the per-part breakdown."""
     parts = {}
     for l in range(w.num_layers if w.window else 1):
         if w.window and l in w.window_layers():
             p = {"window_" + k: v for k, v in layer_bytes(w, seq_lens, "window").items()}
         else:
-            p = layer_bytes(w, seq_lens, "sparse" if sparse else "full")
+            p = layer_bytes(w, seq_lens, "sparse" if sparse else "full", scale_format)
         for k, v in p.items():
             parts[k] = parts.get(k, 0) + v
     return sum(parts.values()), parts
@@ -156,13 +160,13 @@ class Layer:
         self.__dict__.update(kw)
 
 
-def setup(w, device, replicas):
+def setup(w, device, replicas, scale_format="fp32"):
     """Returns (shape, layers of every replica, block_table, seq_lens, generated case)."""
     import torch
     import long_context_decode_amd as L
     from synth import make_gqa_case, make_mla_case
 
-    shape = L.shape_for(w)
+    shape = L.shape_for(w, scale_format=L.SCALE_FORMATS[scale_format])
     if w.kind == "mla":
         M = calibrate_mla(L, w, device)
         case = make_mla_case(w, device=device)
@@ -418,6 +422,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=-1,
                     help="sequences in the CPU-oracle sample (0: skip; default 6 on the default workload)")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing")
+    ap.add_argument("--scale-format", default="fp32", choices=["fp32", "e8m0", "none"],
+                    help="scoring-cache scale: fp32 per token (default), one-byte power of two, or none")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reference for counter scaling)")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -456,12 +462,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     seq = [w.seq_len] * w.batch
-    total_bytes, parts = step_bytes(w, seq, True)
+    total_bytes, parts = step_bytes(w, seq, True, args.scale_format)
     full_bytes, _ = step_bytes(w, seq, False)
     n_rep = args.replicas or (1 if total_bytes > (1 << 30) else 3)
 
     t_setup = time.perf_counter()
-    shape, reps, bt, sl, case = setup(w, dev, n_rep)
+    shape, reps, bt, sl, case = setup(w, dev, n_rep, args.scale_format)
     print(f"[bench] {w.name}: setup {time.perf_counter() - t_setup:.1f} s, {n_rep} replica(s)", file=sys.stderr,
           flush=True)
     ws = L.alloc_workspace(shape, dev)
@@ -538,11 +544,12 @@ def main():
         torch.cuda.synchronize()
     del src, dst
 
-    lb = layer_bytes(w, seq, "sparse")
+    lb = layer_bytes(w, seq, "sparse", args.scale_format)
     stream_bytes = lb["score"]
     achieved = stream_bytes / (stage_ms["select_stream"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(w.name),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for(w.name) if args.scale_format == "fp32" else None,
                 "kernel": "select_stream (FP8 score stream + candidate compaction)",
                 "bytes_per_launch": stream_bytes, "avg_launch_ms": round(stage_ms["select_stream"], 5)}
 
@@ -557,12 +564,15 @@ def main():
         extra["mla_full"] = {"flops": ffl, "tflops": round(ffl / (ms_full * 1e-3) / 1e12, 1),
                              "mfma_bf16_frac": round(ffl / (ms_full * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
-    n_cpu = args.cpu_seqs if args.cpu_seqs >= 0 else (6 if w.name == "llama8b_128k" else 0)
+    n_cpu = args.cpu_seqs if args.cpu_seqs >= 0 else (6 if w.name == "llama8b_128k" and args.scale_format == "fp32"
+                                                       else 0)
     cpu = cpu_baseline(w, case, min(n_cpu, w.batch)) if n_cpu > 0 and not w.window else None
 
     cfg = {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
            "head_dim": w.head_dim, "seq_len": w.seq_len, "page_size": w.page_size, "rank": w.rank,
-           "budget": w.budget, "kv_dtype": "bf16", "scoring_cache": "fp8 e4m3fn + fp32 scale per token",
+           "budget": w.budget, "kv_dtype": "bf16",
+           "scoring_cache": {"fp32": "fp8 e4m3fn + fp32 scale per token", "e8m0": "fp8 e4m3fn + e8m0 scale byte",
+                             "none": "fp8 e4m3fn, no scale"}[args.scale_format],
            "replicas": n_rep}
     if w.window:
         cfg.update(layers=w.num_layers, window=w.window, window_layers=list(w.window_layers()))

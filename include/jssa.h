@@ -41,9 +41,14 @@
  *   kp       uint8 [num_pages, Hkv, S/16, page, 16]   (S = scoring dims:
  *            r for GQA, r + 64 for MLA; 16-byte pieces, piece-major inside
  *            one (page, KV head) block so a wavefront reads it contiguously)
- *   kp_scale fp32  [num_pages, Hkv, page]
+ *   kp_scale [num_pages, Hkv, page], by jssa_shape.scale_format:
+ *            JSSA_SCALE_FP32  fp32 scale (the default);
+ *            JSSA_SCALE_E8M0  uint8 E with value 2^(E - 127) (one byte);
+ *            JSSA_SCALE_NONE  no scale array (NULL), codes of y itself
  *   The element i of the projected key of (page p, slot s, head h) is
- *   kp[p][h][i/16][s][i%16] * kp_scale[p][h][s].
+ *   kp[p][h][i/16][s][i%16] * scale(kp_scale[p][h][s]).  The one-byte and
+ *   scale-free forms move the footprint toward the README page's r bytes per
+ *   token and KV head ("Notes").
  */
 #ifndef JSSA_H_
 #define JSSA_H_
@@ -76,6 +81,9 @@ enum { JSSA_KIND_GQA = 0, JSSA_KIND_MLA = 1 };
  *                 (several passes over the FP8 cache; slow, data independent). */
 enum { JSSA_SELECT_AUTO = 0, JSSA_SELECT_EXACT_STREAM = 1 };
 
+/* jssa_shape.scale_format: the scoring cache's per-(token, KV head) scale. */
+enum { JSSA_SCALE_FP32 = 0, JSSA_SCALE_E8M0 = 1, JSSA_SCALE_NONE = 2 };
+
 typedef struct jssa_shape {
   int32_t kind;               /* JSSA_KIND_GQA or JSSA_KIND_MLA */
   int32_t batch;              /* sequences in the step, >= 1 */
@@ -87,6 +95,7 @@ typedef struct jssa_shape {
   int32_t rank;               /* r: GQA r % 16 == 0, r <= min(d, 128); MLA latent rank, 64 */
   int32_t budget;             /* B: 1..4096 */
   int32_t select_mode;        /* JSSA_SELECT_AUTO or JSSA_SELECT_EXACT_STREAM */
+  int32_t scale_format;       /* JSSA_SCALE_FP32 (0), JSSA_SCALE_E8M0 or JSSA_SCALE_NONE */
 } jssa_shape;
 
 /* Human-readable name of a jssa_status value (static string, never NULL). */
@@ -97,8 +106,9 @@ const char* jssa_status_string(int32_t status);
  * page_size).  Writes *bytes; returns a jssa_status. */
 int32_t jssa_workspace_bytes(const jssa_shape* shape, size_t* bytes);
 
-/* Bytes of the projected scoring cache per page (kp) and fp32 scales per page
- * (kp_scale elements), so callers can size both buffers. */
+/* Bytes of the projected scoring cache per page (kp) and scale elements per
+ * page (kp_scale: fp32 for JSSA_SCALE_FP32, bytes for JSSA_SCALE_E8M0, 0 for
+ * JSSA_SCALE_NONE), so callers can size both buffers. */
 int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page,
                            int64_t* scale_elems_per_page);
 
@@ -107,16 +117,20 @@ int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page,
  *   GQA: y = M_h k (fp32 accumulate); MLA: y = [M c ; k_pe] (128 dims).
  *   scale = max_i |y_i| / 448 (fp32), codes = E4M3FN(y / scale), round to
  *   nearest even, saturating; an all-zero y stores scale 0 and zero codes.
+ *   JSSA_SCALE_E8M0: the scale is rounded up to a power of two 2^e (e = ceil
+ *   log2 of the fp32 scale, clamped to [-127, 127]; stored byte e + 127, 0 for
+ *   a zero row) and codes = E4M3FN(y / 2^e); JSSA_SCALE_NONE: codes = E4M3FN(y).
  * k_new : GQA bf16 [T, Hkv, d]; MLA bf16 [T, 576]
  * slot  : int32 [T], physical page * page_size + slot in page; < 0 skips the row
  * M     : GQA fp32 [Hkv, r, d]; MLA fp32 [r, 512]
- * kp, kp_scale : the scoring cache (layout above), written at the slots only. */
+ * kp, kp_scale : the scoring cache (layout above), written at the slots only
+ *                (kp_scale may be NULL with JSSA_SCALE_NONE). */
 int32_t jssa_store(const jssa_shape* shape, const uint16_t* k_new, const int32_t* slot, int32_t T,
-                   const float* M, uint8_t* kp, float* kp_scale, hipStream_t stream);
+                   const float* M, uint8_t* kp, void* kp_scale, hipStream_t stream);
 
 /* jssa_select — per (sequence b, KV head h): qbar = mean of the G query heads
  * of h (heads h*G .. h*G+G-1), qhat = M_h qbar (fp32; MLA: [M qbar[:512];
- * qbar[512:]]), score s_t = kp_scale_t * sum_i qhat_i * kp_t,i (fp32) for
+ * qbar[512:]]), score s_t = scale_t * sum_i qhat_i * kp_t,i (fp32) for
  * every position t < seq_lens[b], then the min(B, N) positions with the
  * largest score (summary page §3.1 steps 1-2, Eq. 1).  Ties at the B-th
  * score go to the lowest position; -0 counts as +0.
@@ -124,7 +138,7 @@ int32_t jssa_store(const jssa_shape* shape, const uint16_t* k_new, const int32_t
  * scores_out: optional out fp32 [batch, Hkv, max_pages_per_seq*page] (NULL: not
  *             written); positions >= seq_lens[b] are left untouched. */
 int32_t jssa_select(const jssa_shape* shape, const uint16_t* q, const float* M, const uint8_t* kp,
-                    const float* kp_scale, const int32_t* block_table, const int32_t* seq_lens,
+                    const void* kp_scale, const int32_t* block_table, const int32_t* seq_lens,
                     int32_t* indices, float* scores_out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
@@ -138,7 +152,7 @@ int32_t jssa_select(const jssa_shape* shape, const uint16_t* q, const float* M, 
  * stream with the same arguments.  Other arguments as jssa_select. */
 enum { JSSA_STAGE_PROLOGUE = 1, JSSA_STAGE_STREAM = 2, JSSA_STAGE_FINISH = 4, JSSA_STAGE_ALL = 7 };
 int32_t jssa_select_stages(const jssa_shape* shape, int32_t stages, const uint16_t* q, const float* M,
-                           const uint8_t* kp, const float* kp_scale, const int32_t* block_table,
+                           const uint8_t* kp, const void* kp_scale, const int32_t* block_table,
                            const int32_t* seq_lens, int32_t* indices, float* scores_out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
@@ -161,7 +175,7 @@ int32_t jssa_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
  * one new key per sequence (T = batch), i.e. the token at position
  * seq_lens[b]-1, so the token being decoded is itself eligible for selection. */
 int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_new,
-                    const int32_t* slot_new, const float* M, uint8_t* kp, float* kp_scale,
+                    const int32_t* slot_new, const float* M, uint8_t* kp, void* kp_scale,
                     const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* block_table,
                     const int32_t* seq_lens, int32_t* indices, float sm_scale, uint16_t* out,
                     float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_PKG, "libjssa.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 KIND_GQA, KIND_MLA = 0, 1
 SELECT_AUTO, SELECT_EXACT_STREAM = 0, 1
+SCALE_FP32, SCALE_E8M0, SCALE_NONE = 0, 1, 2
+SCALE_FORMATS = {"fp32": SCALE_FP32, "e8m0": SCALE_E8M0, "none": SCALE_NONE}
 STAGE_PROLOGUE, STAGE_STREAM, STAGE_FINISH, STAGE_ALL = 1, 2, 4, 7
 MLA_LATENT, MLA_ROPE = 512, 64
 
@@ -39,7 +41,7 @@ class JSSAError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kind", "batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "max_pages_per_seq",
-        "rank", "budget", "select_mode")]
+        "rank", "budget", "select_mode", "scale_format")]
 
     @property
     def group(self) -> int:
@@ -95,16 +97,18 @@ def _check(fn: str, status: int) -> None:
 
 
 def make_shape(kind: int, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
-               max_pages_per_seq: int, rank: int, budget: int, select_mode: int = SELECT_AUTO) -> Shape:
+               max_pages_per_seq: int, rank: int, budget: int, select_mode: int = SELECT_AUTO,
+               scale_format: int = SCALE_FP32) -> Shape:
     return Shape(kind, batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, rank, budget,
-                 select_mode)
+                 select_mode, scale_format)
 
 
 def shape_for(w, select_mode: int = SELECT_AUTO, batch: Optional[int] = None,
-              max_pages_per_seq: Optional[int] = None) -> Shape:
+              max_pages_per_seq: Optional[int] = None, scale_format: int = SCALE_FP32) -> Shape:
     """Shape of a synth Workload (duck-typed: any object with the same fields)."""
     return make_shape(KIND_MLA if w.kind == "mla" else KIND_GQA, batch or w.batch, w.num_q_heads, w.num_kv_heads,
-                      w.head_dim, w.page_size, max_pages_per_seq or w.pages_per_seq, w.rank, w.budget, select_mode)
+                      w.head_dim, w.page_size, max_pages_per_seq or w.pages_per_seq, w.rank, w.budget, select_mode,
+                      scale_format)
 
 
 def workspace_bytes(shape: Shape) -> int:
@@ -125,11 +129,17 @@ def alloc_workspace(shape: Shape, device="cuda") -> torch.Tensor:
     return torch.empty(workspace_bytes(shape), dtype=torch.uint8, device=device)
 
 
-def alloc_scoring_cache(shape: Shape, num_pages: int, device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
-    """Zeroed projected scoring cache: kp uint8 [num_pages, Hkv, S/16, page, 16], scale fp32 [num_pages, Hkv, page]."""
+def _scale_dtype(shape: Shape):
+    return {SCALE_FP32: torch.float32, SCALE_E8M0: torch.uint8}.get(shape.scale_format)
+
+
+def alloc_scoring_cache(shape: Shape, num_pages: int, device="cuda") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Zeroed projected scoring cache: kp uint8 [num_pages, Hkv, S/16, page, 16] and the scales
+    [num_pages, Hkv, page] (fp32, or uint8 E8M0 bytes; None when the format has no scale)."""
     s = shape.score_dims
     kp = torch.zeros((num_pages, shape.num_kv_heads, s // 16, shape.page_size, 16), dtype=torch.uint8, device=device)
-    sc = torch.zeros((num_pages, shape.num_kv_heads, shape.page_size), dtype=torch.float32, device=device)
+    dt = _scale_dtype(shape)
+    sc = None if dt is None else torch.zeros((num_pages, shape.num_kv_heads, shape.page_size), dtype=dt, device=device)
     return kp, sc
 
 
@@ -169,11 +179,17 @@ def _m_shape(shape: Shape):
     return (shape.num_kv_heads, shape.rank, shape.head_dim)
 
 
-def _kp_args(shape: Shape, kp: torch.Tensor, kp_scale: torch.Tensor):
+def _kp_args(shape: Shape, kp: torch.Tensor, kp_scale: Optional[torch.Tensor]):
     n = kp.shape[0]
     s = shape.score_dims
-    return (_ptr("kp", kp, torch.uint8, (n, shape.num_kv_heads, s // 16, shape.page_size, 16)),
-            _ptr("kp_scale", kp_scale, torch.float32, (n, shape.num_kv_heads, shape.page_size)))
+    dt = _scale_dtype(shape)
+    if dt is None:
+        if kp_scale is not None:
+            raise ValueError("kp_scale: this scale format stores no scale (pass None)")
+        sc = ctypes.c_void_p(0)
+    else:
+        sc = _ptr("kp_scale", kp_scale, dt, (n, shape.num_kv_heads, shape.page_size))
+    return (_ptr("kp", kp, torch.uint8, (n, shape.num_kv_heads, s // 16, shape.page_size, 16)), sc)
 
 
 def _ws(shape: Shape, workspace: torch.Tensor):
@@ -191,7 +207,7 @@ def _table_args(shape: Shape, block_table: torch.Tensor, seq_lens: torch.Tensor)
 # ---------------------------------------------------------------- entry points
 
 def jssa_store(shape: Shape, k_new: torch.Tensor, slot: torch.Tensor, M: torch.Tensor, kp: torch.Tensor,
-               kp_scale: torch.Tensor, check_slots: bool = True) -> None:
+               kp_scale: Optional[torch.Tensor], check_slots: bool = True) -> None:
     """check_slots=True reads the slots back to the host (a synchronisation) to bound-check them."""
     T = int(slot.shape[0])
     kshape = (T, shape.head_dim) if shape.kind == KIND_MLA else (T, shape.num_kv_heads, shape.head_dim)
@@ -204,7 +220,7 @@ def jssa_store(shape: Shape, k_new: torch.Tensor, slot: torch.Tensor, M: torch.T
     _check("jssa_store", _lib.jssa_store(ctypes.byref(shape), *args, _stream()))
 
 
-def jssa_select(shape: Shape, q: torch.Tensor, M: torch.Tensor, kp: torch.Tensor, kp_scale: torch.Tensor,
+def jssa_select(shape: Shape, q: torch.Tensor, M: torch.Tensor, kp: torch.Tensor, kp_scale: Optional[torch.Tensor],
                 block_table: torch.Tensor, seq_lens: torch.Tensor, indices: torch.Tensor,
                 workspace: torch.Tensor, scores_out: Optional[torch.Tensor] = None,
                 stages: Optional[int] = None) -> None:
@@ -239,7 +255,7 @@ def jssa_attend(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: O
 
 
 def jssa_decode(shape: Shape, q: torch.Tensor, k_new: Optional[torch.Tensor], slot_new: Optional[torch.Tensor],
-                M: torch.Tensor, kp: torch.Tensor, kp_scale: torch.Tensor, k_cache: torch.Tensor,
+                M: torch.Tensor, kp: torch.Tensor, kp_scale: Optional[torch.Tensor], k_cache: torch.Tensor,
                 v_cache: Optional[torch.Tensor], block_table: torch.Tensor, seq_lens: torch.Tensor,
                 indices: torch.Tensor, sm_scale: float, out: torch.Tensor, workspace: torch.Tensor,
                 lse_out: Optional[torch.Tensor] = None) -> None:

@@ -18,7 +18,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
-  int kind, batch, Hq, Hkv, d, P, max_pages, r, S, B, G, mla, dv;
+  int kind, batch, Hq, Hkv, d, P, max_pages, r, S, B, G, mla, dv, sfmt;
   int64_t maxN;
   int cp, max_chunks;
   int sp_splits, sp_len;     // sparse attention split plan
@@ -69,6 +69,9 @@ int32_t validate_shape(const jssa_shape* sh) {
   if (sh->budget < 1 || sh->budget > 4096) return JSSA_ERR_SHAPE;
   if (sh->page_size != 16 && sh->page_size != 32 && sh->page_size != 64) return JSSA_ERR_UNSUPPORTED;
   if (sh->select_mode != JSSA_SELECT_AUTO && sh->select_mode != JSSA_SELECT_EXACT_STREAM) return JSSA_ERR_SHAPE;
+  if (sh->scale_format != JSSA_SCALE_FP32 && sh->scale_format != JSSA_SCALE_E8M0 &&
+      sh->scale_format != JSSA_SCALE_NONE)
+    return JSSA_ERR_UNSUPPORTED;
   if (sh->rank < 16 || sh->rank % 16 != 0) return JSSA_ERR_UNSUPPORTED;
   if (sh->kind == JSSA_KIND_GQA) {
     if (sh->head_dim != 128 && sh->head_dim != 256) return JSSA_ERR_UNSUPPORTED;
@@ -88,6 +91,7 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   if (st != JSSA_OK) return st;
   p->kind = sh->kind;
   p->mla = sh->kind == JSSA_KIND_MLA;
+  p->sfmt = sh->scale_format;
   p->batch = sh->batch;
   p->Hq = sh->num_q_heads;
   p->Hkv = sh->num_kv_heads;
@@ -148,10 +152,10 @@ T* at(void* ws, size_t off) {
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? JSSA_OK : JSSA_ERR_HIP; }
 
 int32_t do_store(const Plan& p, const uint16_t* k_new, const int32_t* slot, int32_t T, const float* M,
-                 uint8_t* kp, float* kp_scale, hipStream_t stream) {
+                 uint8_t* kp, void* kp_scale, hipStream_t stream) {
   if (T < 0) return JSSA_ERR_SHAPE;
   if (T == 0) return JSSA_OK;
-  if (!k_new || !slot || !M || !kp || !kp_scale) return JSSA_ERR_NULL;
+  if (!k_new || !slot || !M || !kp || (!kp_scale && p.sfmt != JSSA_SCALE_NONE)) return JSSA_ERR_NULL;
   StoreArgs a{};
   a.k_new = k_new;
   a.slot = slot;
@@ -165,20 +169,23 @@ int32_t do_store(const Plan& p, const uint16_t* k_new, const int32_t* slot, int3
   a.r = p.r;
   a.S = p.S;
   a.mla = p.mla;
+  a.sfmt = p.sfmt;
   return hip_status(launch_store(a, stream));
 }
 
 int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q, const float* M, const uint8_t* kp,
-                  const float* kp_scale, const int32_t* block_table, const int32_t* seq_lens, int32_t* indices,
+                  const void* kp_scale, const int32_t* block_table, const int32_t* seq_lens, int32_t* indices,
                   float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream, const uint16_t* k_new = nullptr,
                   const int32_t* slot_new = nullptr) {
-  if (!q || !M || !kp || !kp_scale || !block_table || !seq_lens || !indices || !ws) return JSSA_ERR_NULL;
+  if (!q || !M || !kp || (!kp_scale && p.sfmt != JSSA_SCALE_NONE) || !block_table || !seq_lens || !indices || !ws)
+    return JSSA_ERR_NULL;
   if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
   SelectArgs a{};
   a.q = q;
   a.M = M;
   a.kp = kp;
   a.kp_scale = kp_scale;
+  a.sfmt = p.sfmt;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.indices = indices;
@@ -290,12 +297,12 @@ int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page, 
   const int32_t st = make_plan(shape, &p);
   if (st != JSSA_OK) return st;
   *kp_bytes_per_page = (int64_t)p.Hkv * p.P * p.S;
-  *scale_elems_per_page = (int64_t)p.Hkv * p.P;
+  *scale_elems_per_page = p.sfmt == JSSA_SCALE_NONE ? 0 : (int64_t)p.Hkv * p.P;
   return JSSA_OK;
 }
 
 int32_t jssa_store(const jssa_shape* shape, const uint16_t* k_new, const int32_t* slot, int32_t T, const float* M,
-                   uint8_t* kp, float* kp_scale, hipStream_t stream) {
+                   uint8_t* kp, void* kp_scale, hipStream_t stream) {
   Plan p;
   const int32_t st = make_plan(shape, &p);
   if (st != JSSA_OK) return st;
@@ -303,7 +310,7 @@ int32_t jssa_store(const jssa_shape* shape, const uint16_t* k_new, const int32_t
 }
 
 int32_t jssa_select(const jssa_shape* shape, const uint16_t* q, const float* M, const uint8_t* kp,
-                    const float* kp_scale, const int32_t* block_table, const int32_t* seq_lens, int32_t* indices,
+                    const void* kp_scale, const int32_t* block_table, const int32_t* seq_lens, int32_t* indices,
                     float* scores_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan p;
   const int32_t st = make_plan(shape, &p);
@@ -313,7 +320,7 @@ int32_t jssa_select(const jssa_shape* shape, const uint16_t* q, const float* M, 
 }
 
 int32_t jssa_select_stages(const jssa_shape* shape, int32_t stages, const uint16_t* q, const float* M,
-                           const uint8_t* kp, const float* kp_scale, const int32_t* block_table,
+                           const uint8_t* kp, const void* kp_scale, const int32_t* block_table,
                            const int32_t* seq_lens, int32_t* indices, float* scores_out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
   Plan p;
@@ -336,14 +343,15 @@ int32_t jssa_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
 }
 
 int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_new, const int32_t* slot_new,
-                    const float* M, uint8_t* kp, float* kp_scale, const uint16_t* k_cache, const uint16_t* v_cache,
+                    const float* M, uint8_t* kp, void* kp_scale, const uint16_t* k_cache, const uint16_t* v_cache,
                     const int32_t* block_table, const int32_t* seq_lens, int32_t* indices, float sm_scale,
                     uint16_t* out, float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan p;
   int32_t st = make_plan(shape, &p);
   if (st != JSSA_OK) return st;
   // validate everything before the first launch
-  if (!q || !M || !kp || !kp_scale || !k_cache || !block_table || !seq_lens || !indices || !out || !workspace)
+  if (!q || !M || !kp || (!kp_scale && p.sfmt != JSSA_SCALE_NONE) || !k_cache || !block_table || !seq_lens ||
+      !indices || !out || !workspace)
     return JSSA_ERR_NULL;
   if (!p.mla && !v_cache) return JSSA_ERR_NULL;
   if (k_new && !slot_new) return JSSA_ERR_NULL;

@@ -81,6 +81,50 @@ __device__ __forceinline__ float proj_combine(float v) {
   return v;
 }
 
+// Scale of one projected key (scoring-cache format sfmt: 0 fp32, 1 E8M0, 2
+// none).  Returns the divisor of y (0 for an all-zero row of a scaled format)
+// and the stored representation: fp32 bits, the E8M0 byte e + 127 with
+// e = ceil(log2(amax / 448)) clamped to [-127, 127], or nothing.
+__device__ __forceinline__ float quant_divisor(float amax, int sfmt, uint32_t* stored) {
+  if (sfmt == 2) {
+    *stored = 0u;
+    return 1.0f;
+  }
+  const float s = amax / 448.0f;
+  if (sfmt == 0) {
+    *stored = __float_as_uint(s);
+    return s;
+  }
+  if (!(s > 0.0f)) {
+    *stored = 0u;
+    return 0.0f;
+  }
+  int e;
+  const float m = frexpf(s, &e);          // s = m 2^e, m in [0.5, 1)
+  if (m == 0.5f) e -= 1;                   // s is itself 2^(e-1)
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  *stored = (uint32_t)(e + 127);
+  return ldexpf(1.0f, e);                  // exact (2^-127 is an fp32 subnormal)
+}
+
+__device__ __forceinline__ void store_scale(void* base, int64_t i, int sfmt, uint32_t stored) {
+  if (sfmt == 0) static_cast<float*>(base)[i] = __uint_as_float(stored);
+  else if (sfmt == 1) static_cast<uint8_t*>(base)[i] = (uint8_t)stored;
+}
+
+// The factor a score is multiplied by: the fp32 scale, 2^(E - 127), or 1.
+// (E8M0 scale arrays start 4-byte aligned; the word of element i lies inside
+// the array because the page size is a multiple of 4.)
+__device__ __forceinline__ float load_scale(const void* base, int64_t i, int sfmt) {
+  if (sfmt == 0) return static_cast<const float*>(base)[i];
+  if (sfmt == 1) {       // the aligned word holding the byte (four lanes share one load)
+    const uint32_t w = static_cast<const uint32_t*>(base)[i >> 2];
+    const uint32_t b = (w >> ((i & 3) * 8)) & 0xffu;
+    return __uint_as_float(b ? (b << 23) : 0x00400000u);
+  }
+  return 1.0f;
+}
+
 // Byte offset of element o of the projected key at (page, head, slot) in the
 // piece-major scoring cache [pages][Hkv][S/16][P][16].
 __device__ __forceinline__ int64_t kp_offset(int64_t page, int head, int slot, int o, int Hkv, int S, int P) {

@@ -18,15 +18,16 @@ struct StoreArgs {
   const int32_t* slot;
   const float* M;
   uint8_t* kp;
-  float* kp_scale;
+  void* kp_scale;          // fp32 / E8M0 bytes / unused, by sfmt
   int T, Hkv, P, d, r, S, mla;
+  int sfmt;                // 0 fp32 scale, 1 E8M0 byte, 2 none
 };
 
 struct SelectArgs {
   const uint16_t* q;
   const float* M;
   const uint8_t* kp;
-  const float* kp_scale;
+  const void* kp_scale;    // fp32 / E8M0 bytes / unused, by sfmt
   const int32_t* block_table;
   const int32_t* seq_lens;
   int32_t* indices;
@@ -43,6 +44,7 @@ struct SelectArgs {
   int cp;               // pages per stream chunk (4 groups of 16 / (scoring dims / 16))
   int max_chunks;
   int force_exact;
+  int sfmt;             // 0 fp32 scale, 1 E8M0 byte, 2 none
 };
 
 struct AttendArgs {

@@ -160,7 +160,17 @@ __device__ __forceinline__ void load_token(const SelectArgs& a, int64_t phys, in
   const uint8_t* base = a.kp + (phys * a.Hkv + head) * ((int64_t)R * 16 * a.P) + slot * 16;
 #pragma unroll
   for (int j = 0; j < R; ++j) pc[j] = *reinterpret_cast<const uint4*>(base + (int64_t)j * a.P * 16);
-  sc = a.kp_scale[(phys * a.Hkv + head) * a.P + slot];
+  sc = load_scale(a.kp_scale, (phys * a.Hkv + head) * a.P + slot, a.sfmt);
+}
+
+// load_token with the scale format fixed at compile time (the stream kernel).
+template <int R, int SF>
+__device__ __forceinline__ void load_token_sf(const SelectArgs& a, int64_t phys, int head, int slot, uint4 (&pc)[R],
+                                              float& sc) {
+  const uint8_t* base = a.kp + (phys * a.Hkv + head) * ((int64_t)R * 16 * a.P) + slot * 16;
+#pragma unroll
+  for (int j = 0; j < R; ++j) pc[j] = *reinterpret_cast<const uint4*>(base + (int64_t)j * a.P * 16);
+  sc = load_scale(a.kp_scale, (phys * a.Hkv + head) * a.P + slot, SF);
 }
 
 template <int R>
@@ -342,13 +352,14 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     float am = 0.0f;
     for (int o = tid; o < S; o += 64) am = fmaxf(am, fabsf(ynew[o]));
     am = wave_max(am);
-    const float scale = am / 448.0f;
+    uint32_t stored;
+    const float div = quant_divisor(am, a.sfmt, &stored);
     const int page = new_slot / a.P, sip = new_slot % a.P;
     for (int o = tid; o < S; o += 64) {
-      const uint32_t code = (scale > 0.0f) ? f32_to_fp8(ynew[o] / scale) : 0u;
+      const uint32_t code = (div > 0.0f) ? f32_to_fp8(ynew[o] / div) : 0u;
       const_cast<uint8_t*>(a.kp)[kp_offset(page, h, sip, o, a.Hkv, S, a.P)] = (uint8_t)code;
     }
-    if (tid == 0) const_cast<float*>(a.kp_scale)[((int64_t)page * a.Hkv + h) * a.P + sip] = scale;
+    if (tid == 0) store_scale(const_cast<void*>(a.kp_scale), ((int64_t)page * a.Hkv + h) * a.P + sip, a.sfmt, stored);
   }
   __syncthreads();
 
@@ -386,7 +397,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 
 // ================================================================== 2. stream
 
-template <int R, int P>
+template <int R, int P, int SF>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(R <= 2 ? 4 : 1))) void select_stream(SelectArgs a) {
   constexpr int S = R * 16;
   constexpr int HPW = 64 / P;               // KV heads covered by one wavefront
@@ -413,7 +424,7 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int f = 0; f < PF; ++f) {
     const int64_t phys = __builtin_amdgcn_readlane(phys_l, f);
-    if (active && page0 + f < n_pages) load_token<R>(a, phys, head, slot, pc[f], sc[f]);
+    if (active && page0 + f < n_pages) load_token_sf<R, SF>(a, phys, head, slot, pc[f], sc[f]);
   }
   float qh[S];
   {
@@ -653,7 +664,13 @@ hipError_t launch_select_rp(const SelectArgs& a, int stages, hipStream_t s) {
   }
   if (stages & 2) {
     const int hg = (a.Hkv + HPW - 1) / HPW;
-    hipLaunchKernelGGL((select_stream<R, P>), dim3(hg, a.max_chunks, a.batch), dim3(kStreamThreads), 0, s, a);
+    const dim3 grid(hg, a.max_chunks, a.batch);
+    if (a.sfmt == 1)
+      hipLaunchKernelGGL((select_stream<R, P, 1>), grid, dim3(kStreamThreads), 0, s, a);
+    else if (a.sfmt == 2)
+      hipLaunchKernelGGL((select_stream<R, P, 2>), grid, dim3(kStreamThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((select_stream<R, P, 0>), grid, dim3(kStreamThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4) {

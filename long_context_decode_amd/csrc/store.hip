@@ -3,6 +3,8 @@
 // scoring cache (paper summary page, §3.4 Projected Scoring Cache:
 // K_proj = K M^T kept in FP8; MLA scores on 64 latent + 64 RoPE dims).
 //
+// The scale format (fp32, one-byte power of two, none) follows the shape.
+//
 // One wavefront per (new token, KV head).  The projected outputs are done
 // eight at a time: lane l takes part l & 7 of output 8 pass + (l >> 3)
 // (project_part / proj_combine); the MLA RoPE dims pass through, one per
@@ -47,20 +49,21 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
     amax = fmaxf(amax, fabsf(yr));
   }
   amax = wave_max(amax);
-  const float scale = amax / 448.0f;
+  uint32_t stored;
+  const float div = quant_divisor(amax, a.sfmt, &stored);
 
 #pragma unroll
   for (int p = 0; p < kMaxPasses; ++p) {
     if (p < passes && part == 0) {
-      const uint32_t code = (scale > 0.0f) ? f32_to_fp8(y[p] / scale) : 0u;
+      const uint32_t code = (div > 0.0f) ? f32_to_fp8(y[p] / div) : 0u;
       a.kp[kp_offset(page, h, sip, p * 8 + oi, a.Hkv, a.S, a.P)] = (uint8_t)code;
     }
   }
   if (a.mla) {
-    const uint32_t code = (scale > 0.0f) ? f32_to_fp8(yr / scale) : 0u;
+    const uint32_t code = (div > 0.0f) ? f32_to_fp8(yr / div) : 0u;
     a.kp[kp_offset(page, h, sip, a.r + lane, a.Hkv, a.S, a.P)] = (uint8_t)code;
   }
-  if (lane == 0) a.kp_scale[((int64_t)page * a.Hkv + h) * a.P + sip] = scale;
+  if (lane == 0) store_scale(a.kp_scale, ((int64_t)page * a.Hkv + h) * a.P + sip, a.sfmt, stored);
 }
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
