@@ -40,7 +40,7 @@ void split_plan(int64_t n_tok_max, int pairs, int* splits, int* len) {
   }
   int64_t s = cdiv(512, std::max(pairs, 1));
   s = std::min<int64_t>(s, cdiv(n_tok_max, 256));
-  s = std::max<int64_t>(1, std::min<int64_t>(s, 256));
+  s = std::max<int64_t>(1, std::min<int64_t>(s, 64));    // 4 partials per split, at most 256 per head
   const int64_t l = cdiv(cdiv(n_tok_max, s), 256) * 256;
   *len = (int)l;
   *splits = (int)cdiv(n_tok_max, l);
@@ -123,8 +123,6 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   int st_splits, st_len;                    // dense attention over the staging cache
   if (p->mla) mla_dense_plan((int64_t)p->stage_pages * p->P, p->batch, p->Hq, &st_splits, &st_len);
   else split_plan((int64_t)p->stage_pages * p->P, p->batch * p->Hkv, &st_splits, &st_len);
-  const int max_splits =
-      std::max({p->sp_splits, p->dn_splits, st_splits, p->mla ? std::max(p->ml_splits, p->md_splits) : 1});
   const size_t bh = (size_t)p->batch * p->Hkv;
   const size_t cand = bh * p->max_chunks * p->cp * p->P;   // one region per stream chunk
   size_t off = 0;
@@ -132,7 +130,10 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   p->off_tau = off;     off = align_up(off + bh * sizeof(uint32_t));
   p->off_chunk = off;   off = align_up(off + bh * p->max_chunks * sizeof(int32_t));
   p->off_cand = off;    off = align_up(off + cand * 2 * sizeof(uint32_t));
-  const size_t pj = (size_t)p->batch * p->Hq * max_splits;
+  const int gqa_splits = std::max({p->sp_splits, p->dn_splits, st_splits});
+  // split-K partials: one per block for MLA, one per wavefront (4 per split) for GQA
+  const size_t parts = p->mla ? (size_t)std::max({p->ml_splits, p->md_splits, st_splits}) : (size_t)gqa_splits * 4;
+  const size_t pj = (size_t)p->batch * p->Hq * parts;
   p->off_part_o = off;  off = align_up(off + pj * p->dv * sizeof(float));
   p->off_part_ml = off; off = align_up(off + pj * 2 * sizeof(float));
   const size_t stage_rows = (size_t)p->batch * p->stage_pages * p->P * p->Hkv;
@@ -239,6 +240,7 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
   a.B = p.B;
   a.G = p.G;
   a.window = indices ? 0 : window;
+  a.parts = p.mla ? 1 : 4;
   if (p.mla) {
     if (indices) {
       a.splits = p.ml_splits;

@@ -18,7 +18,7 @@
 //   B. one softmax update per batch: the wave max of the 64 logits, a single
 //      rescale of the running state, p = 2^(x - m) per lane;
 //   C. the V rows are requested in groups of 8 and o += p v, p broadcast along
-//      the row with a lane permute.
+//      the row with DPP (row_newbcast).
 // Each loaded row serves all G query heads of the KV head.  The running max is
 // uniform over the wavefront, so the rows' partial sums add directly; waves
 // merge in LDS, splits in merge_kernel.  DENSE instantiates the full-KV /
@@ -63,9 +63,11 @@ __global__ __launch_bounds__(256) void merge_kernel(AttendArgs a) {
   int n_tok;
   if (a.indices) n_tok = N < a.B ? N : a.B;
   else n_tok = (a.window > 0 && N > a.window) ? a.window : N;
-  const int ns = min(a.splits, (n_tok + a.split_len - 1) / a.split_len);
-  const int64_t pj0 = ((int64_t)b * a.Hq + j) * a.splits;
-  // splits <= 256: thread s holds split s
+  // partials of the splits that hold positions (a.parts per split: one per
+  // wavefront for the GQA kernel, one per block for the MLA kernel)
+  const int ns = min(a.splits, (n_tok + a.split_len - 1) / a.split_len) * a.parts;
+  const int64_t pj0 = ((int64_t)b * a.Hq + j) * ((int64_t)a.splits * a.parts);
+  // at most 256 partials: thread s holds partial s
   float ms_ = -INFINITY, ls_ = 0.0f;
   if (tid < ns) {
     ls_ = a.part_ml[(pj0 + tid) * 2 + 1];
@@ -107,9 +109,8 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   constexpr int EPL = D / 16;   // elements per lane
   constexpr int NV = EPL / 8;   // 16-byte loads per lane per row
   constexpr int NP = EPL / 2;   // bf16 pairs per lane per row
-  constexpr int GRP = 8 / NV;   // rows whose loads are in flight together (32 VGPRs)
-  __shared__ float red_o[4][G][D];
-  __shared__ float red_ml[4][G][2];
+  constexpr int GRP = 8 / NV;   // V rows whose loads are in flight together (32 VGPRs)
+  constexpr int GRPK = 16 / NV; // K rows whose loads are in flight together (64 VGPRs)
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = (int)threadIdx.x, lane = lane_id(), w = tid >> 6;
   const int row = lane >> 4, c16 = lane & 15;
@@ -172,17 +173,17 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) xs[g] = -INFINITY;
 #pragma unroll
-    for (int u0 = 0; u0 < 16; u0 += GRP) {
-      uint4 kr[GRP][NV];
+    for (int u0 = 0; u0 < 16; u0 += GRPK) {
+      uint4 kr[GRPK][NV];
 #pragma unroll
-      for (int u = 0; u < GRP; ++u) {
-        const int rr = __shfl(ri, (lane & 48) + u0 + u);
+      for (int u = 0; u < GRPK; ++u) {
+        const int rr = row_bcast(ri, u0 + u);
         const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
 #pragma unroll
         for (int v = 0; v < NV; ++v) kr[u][v] = *reinterpret_cast<const uint4*>(kbase + ro + v * 8);
       }
 #pragma unroll
-      for (int u = 0; u < GRP; ++u) {
+      for (int u = 0; u < GRPK; ++u) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float acc = 0.0f;
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
       uint4 vr[GRP][NV];
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {
-        const int rr = __shfl(ri, (lane & 48) + u0 + u);
+        const int rr = row_bcast(ri, u0 + u);
         const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
 #pragma unroll
         for (int v = 0; v < NV; ++v) vr[u][v] = *reinterpret_cast<const uint4*>(vbase + ro + v * 8);
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
       for (int u = 0; u < GRP; ++u) {
         float pp[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) pp[g] = __shfl(p[g], (lane & 48) + u0 + u);
+        for (int g = 0; g < G; ++g) pp[g] = row_bcast_f(p[g], u0 + u);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           const uint32_t ww[4] = {vr[u][v].x, vr[u][v].y, vr[u][v].z, vr[u][v].w};
@@ -251,7 +252,8 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
     ri = ri_next;
   }
 
-  // rows share the wave's running max: sum the four rows and the lanes' l
+  // rows share the wave's running max: sum the four rows and the lanes' l,
+  // then this wavefront's partial (o, m, l) goes out as partial 4 s + w
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     l[g] = wave_sum(l[g]);
@@ -260,35 +262,16 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
       o[g][e] += __shfl_xor(o[g][e], 16);
       o[g][e] += __shfl_xor(o[g][e], 32);
     }
+    const int64_t pj = ((int64_t)b * a.Hq + (int64_t)h * G + g) * ((int64_t)a.splits * 4) + s * 4 + w;
     if (row == 0) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) red_o[w][g][c16 * EPL + e] = o[g][e];
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(&a.part_o[pj * D + c16 * EPL + e]) =
+            make_float4(o[g][e], o[g][e + 1], o[g][e + 2], o[g][e + 3]);
       if (c16 == 0) {
-        red_ml[w][g][0] = m[g];
-        red_ml[w][g][1] = l[g];
+        a.part_ml[pj * 2] = m[g];
+        a.part_ml[pj * 2 + 1] = l[g];
       }
-    }
-  }
-  __syncthreads();
-  // merge the four wavefronts and write this split's partial
-  for (int k = tid; k < G * D; k += kAttendThreads) {
-    const int g = k / D, dim = k % D;
-    float mm = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, red_ml[ww][g][0]);
-    const float ms = (mm == -INFINITY) ? 0.0f : mm;
-    float acc = 0.0f, ll = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float f = __builtin_amdgcn_exp2f(red_ml[ww][g][0] - ms);
-      acc += red_o[ww][g][dim] * f;
-      ll += red_ml[ww][g][1] * f;
-    }
-    const int64_t pj = ((int64_t)b * a.Hq + (int64_t)h * G + g) * a.splits + s;
-    a.part_o[pj * D + dim] = acc;
-    if (dim == 0) {
-      a.part_ml[pj * 2] = mm;
-      a.part_ml[pj * 2 + 1] = ll;
     }
   }
 }

@@ -179,6 +179,34 @@ __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
+// Lane u (0..15) of every row of 16 lanes, broadcast to the whole row (DPP
+// row_newbcast).  u must be a constant once the caller's loop is unrolled.
+template <int U>
+__device__ __forceinline__ int row_bcast_c(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, 0x150 + U, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int row_bcast(int x, int u) {
+  switch (u) {
+    case 0: return row_bcast_c<0>(x);
+    case 1: return row_bcast_c<1>(x);
+    case 2: return row_bcast_c<2>(x);
+    case 3: return row_bcast_c<3>(x);
+    case 4: return row_bcast_c<4>(x);
+    case 5: return row_bcast_c<5>(x);
+    case 6: return row_bcast_c<6>(x);
+    case 7: return row_bcast_c<7>(x);
+    case 8: return row_bcast_c<8>(x);
+    case 9: return row_bcast_c<9>(x);
+    case 10: return row_bcast_c<10>(x);
+    case 11: return row_bcast_c<11>(x);
+    case 12: return row_bcast_c<12>(x);
+    case 13: return row_bcast_c<13>(x);
+    case 14: return row_bcast_c<14>(x);
+    default: return row_bcast_c<15>(x);
+  }
+}
+__device__ __forceinline__ float row_bcast_f(float x, int u) { return __int_as_float(row_bcast(__float_as_int(x), u)); }
+
 // Sum over each row of 16 lanes (DPP row rotations); every lane of the row
 // receives the row total.
 __device__ __forceinline__ float row16_sum(float x) {

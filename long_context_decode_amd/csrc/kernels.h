@@ -54,13 +54,14 @@ struct AttendArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* indices;  // NULL: dense positions [lo, N)
-  float* part_o;           // [batch, Hq, splits, dv]
-  float* part_ml;          // [batch, Hq, splits, 2]  (running max in log2 units, sum)
+  float* part_o;           // [batch, Hq, splits * parts, dv]
+  float* part_ml;          // [batch, Hq, splits * parts, 2]  (running max in log2 units, sum)
   uint16_t* out;           // [batch, Hq, dv]
   float* lse_out;          // [batch, Hq] or NULL
   float sm_log2;           // sm_scale * log2(e)
   int batch, Hq, Hkv, P, max_pages, B, G, window;
   int splits, split_len;
+  int parts;               // partials per split: 4 (one per wavefront, GQA) or 1 (MLA)
 };
 
 struct GatherArgs {
