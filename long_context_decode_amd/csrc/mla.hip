@@ -39,6 +39,7 @@ namespace jssa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = kMlaLatent + kMlaRope;  // 576
@@ -63,8 +64,13 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
-// K index (0..63) of row t of a tile in the P / V operand order.
-__device__ __forceinline__ int k_of_row(int t) { return (t & 32) + (t & 3) * 8 + ((t & 31) >> 2); }
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane 4k + a supplies the address of 4 consecutive bf16 and lane 4a' + b'
+// receives element b' of the chunks of lanes a', 4 + a', 8 + a', 12 + a' (k = 0..3).
+__device__ __forceinline__ bf16x4 ds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(const_cast<uint16_t*>(p)));
+}
 
 }  // namespace
 
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
       }
     __syncthreads();
     // ---- softmax update (every wavefront computes the same state)
-    const int kpos = k_of_row(w * 16 + c);
+    const int kpos = w * 16 + c;                       // P in natural row order
     float4 rm[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -258,11 +264,14 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
         ap[mt] = *reinterpret_cast<const bf16x8*>(&Ps[(mt * 16 + c) * kPRow + kk * 32 + g * 8]);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const int dim = w * 128 + nt * 16 + c;
-        uint16_t vv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vv[i] = Kt[(kk * 32 + 4 * i + g) * kRow + dim];
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vv));
+        // B operand: rows kk*32 + 8g .. +7 of output dim w*128 + nt*16 + c, two
+        // transposing reads of 4 rows each (lane 4k + a of the group points at
+        // row +k, dims +4a .. +4a+3)
+        const int dim0 = w * 128 + nt * 16 + (c & 3) * 4;
+        const int row0 = kk * 32 + g * 8 + (c >> 2);
+        const bf16x4 v0 = ds_read_tr(&Kt[row0 * kRow + dim0]);
+        const bf16x4 v1 = ds_read_tr(&Kt[(row0 + 4) * kRow + dim0]);
+        const bf16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) O[mt][nt] = mfma16(ap[mt], bv, O[mt][nt]);
       }
