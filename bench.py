@@ -409,6 +409,73 @@ def summarize_trace(d, command):
     return "\n".join(lines) + "\n"
 
 
+# ----------------------------------------------------------------------------- recall sweep
+
+def recall_sweep(name, ranks, n_seqs, query_shift=0):
+    """Top-B recall of the FP8 projected-score selection against the exact top-B of qbar . k (fp32 scores
+    from plain torch on the GPU), for several ranks and three bases per KV head: the joint basis M*
+    (jssa_calib_moments + jssa_basis), the top-r eigenvectors of the key moments alone (jssa_basis with the
+    key moments on both sides) and a random orthonormal basis.  Also reports the planted needles found."""
+    import numpy as np
+    import torch
+    import long_context_decode_amd as L
+    from synth import WORKLOADS, make_gqa_calibration, make_gqa_case
+    from synth.workloads import haar_orthogonal
+
+    w = WORKLOADS[name].scaled(batch=n_seqs, query_shift=query_shift)
+    dev = torch.device("cuda:0")
+    case = make_gqa_case(w, device=dev, layers=[0])
+    lay = case.layers[0]
+    bt, sl = case.block_table.to(dev), case.seq_lens.to(dev)
+    qc, kc = make_gqa_calibration(w, 0, device=dev)
+    # exact top-B per (sequence, KV head) from fp32 scores qbar . k
+    P, N, G = w.page_size, w.seq_len, w.group
+    t = torch.arange(N, device=dev)
+    exact = []
+    for b in range(w.batch):
+        keys = lay.k_cache[bt[b].long()[t // P], t % P].float()                      # [N, Hkv, d]
+        qbar = lay.q[b].float().view(w.num_kv_heads, G, w.head_dim).mean(1)         # [Hkv, d]
+        s = torch.einsum("nhd,hd->hn", keys, qbar)
+        exact.append(torch.topk(s, w.budget, dim=1).indices)                         # [Hkv, B]
+    needles = {k: torch.as_tensor(v, device=dev) for k, v in lay.needles.items()}
+    rows = []
+    for r in ranks:
+        shape = L.shape_for(w.scaled(rank=r))
+        T = qc.shape[0]
+        gq = torch.zeros((w.num_kv_heads, w.head_dim, w.head_dim), dtype=torch.float32, device=dev)
+        gk = torch.zeros_like(gq)
+        L.jssa_calib_moments(shape, qc, kc, gq, gk,
+                             torch.empty(L.calib_workspace_bytes(shape, T), dtype=torch.uint8, device=dev))
+        gq_h, gk_h = gq.cpu().numpy(), gk.cpu().numpy()
+        bases = {
+            "joint M*": L.jssa_basis(shape, gq_h, gk_h),
+            "keys only": L.jssa_basis(shape, gk_h, gk_h),
+            "random": np.stack([haar_orthogonal(w.head_dim, 1000 + 7 * h + r)[:, :r].T
+                                for h in range(w.num_kv_heads)]).astype(np.float32),
+        }
+        for bname, m in bases.items():
+            M = torch.from_numpy(np.ascontiguousarray(m)).to(dev)
+            kp, ks = L.alloc_scoring_cache(shape, lay.k_cache.shape[0], dev)
+            bulk_store(L, w, shape, lay.k_cache.view(-1, w.num_kv_heads, w.head_dim), bt, sl, M, kp, ks)
+            idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=dev)
+            L.jssa_select(shape, lay.q, M, kp, ks, bt, sl, idx, L.alloc_workspace(shape, dev))
+            hits, found, total_n = 0, 0, 0
+            for b in range(w.batch):
+                for h in range(w.num_kv_heads):
+                    sel = idx[b, h].long()
+                    hits += int(torch.isin(sel, exact[b][h]).sum())
+                    nd = needles[(b, h)]
+                    found += int(torch.isin(nd, sel).sum())
+                    total_n += len(nd)
+            rows.append({"rank": r, "basis": bname,
+                         "topB_recall": round(hits / (w.batch * w.num_kv_heads * w.budget), 4),
+                         "needle_recall": round(found / max(total_n, 1), 4)})
+            print(f"[recall] r={r} {bname}: {rows[-1]}", file=sys.stderr, flush=True)
+            del kp, ks
+    return {"workload": w.name, "sequences": w.batch, "seq_len": w.seq_len, "budget": w.budget,
+            "query_shift": query_shift, "scoring_cache": "fp8 e4m3fn + fp32 scale", "rows": rows}
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -426,6 +493,9 @@ def main():
                     help="scoring-cache scale: fp32 per token (default), one-byte power of two, or none")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reference for counter scaling)")
+    ap.add_argument("--recall-sweep", action="store_true",
+                    help="top-B recall vs rank for the joint, key-only and random bases (prints one JSON line)")
+    ap.add_argument("--ranks", default="16,32,48,64")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--command", default="", help="profiling command recorded in a summary")
@@ -446,6 +516,15 @@ def main():
                 f.write(txt)
         else:
             print(txt)
+        return
+
+    if args.recall_sweep:
+        from synth import WORKLOADS
+        w = args.workload if args.workload != "llama8b_128k" else "llama8b_32k"
+        ranks = [int(x) for x in args.ranks.split(",")]
+        # queries sharing the keys' leading directions, then queries whose energy sits half a basis away
+        res = [recall_sweep(w, ranks, 4, shift) for shift in (0, WORKLOADS[w].head_dim // 2)]
+        print(json.dumps(res), flush=True)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -71,6 +71,7 @@ class Workload:
     latent_dim: int = 0        # MLA only
     rope_dim: int = 0          # MLA only
     needle_frac: float = 0.01
+    query_shift: int = 0       # >0: the query spectrum is rolled by this many of the basis' directions
 
     @property
     def group(self) -> int:
@@ -254,7 +255,7 @@ def make_gqa_layer(w: Workload, layer: int, block_table: np.ndarray, seq_lens: n
     q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=device)
     cq = query_amplitude(d, d)
     kfacs = [_factor(w, layer, h, d, key_spectrum(d)) for h in range(Hkv)]
-    qfacs = [_factor(w, layer, h, d, query_spectrum(d)) for h in range(Hkv)]
+    qfacs = [_factor(w, layer, h, d, np.roll(query_spectrum(d), w.query_shift)) for h in range(Hkv)]
     bt = torch.as_tensor(block_table.astype(np.int64), device=device)
     planted = {}
     for b in range(B):
@@ -299,7 +300,7 @@ def make_gqa_calibration(w: Workload, layer: int, device="cpu") -> Tuple[torch.T
     ks = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=device)
     for h in range(Hkv):
         kf = _factor(w, layer, h, d, key_spectrum(d))
-        qf = _factor(w, layer, h, d, query_spectrum(d))
+        qf = _factor(w, layer, h, d, np.roll(query_spectrum(d), w.query_shift))
         ks[:, h] = _draw_rows(T, kf, seed_for(w.model, layer, h, P_CAL_K), device).to(torch.bfloat16)
         for g in range(G):
             j = h * G + g
