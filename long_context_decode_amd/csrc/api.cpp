@@ -47,7 +47,7 @@ void split_plan(int64_t n_tok_max, int pairs, int* splits, int* len) {
 }
 
 // MLA dense split plan: about 512 blocks of (split, 32 heads, sequence), at
-// most 256 splits (the merge holds one split per thread), 64-row tiles.
+// most 256 splits (the merge holds one split per thread), 64-row multiples.
 void mla_dense_plan(int64_t n, int batch, int Hq, int* splits, int* len) {
   if (n <= 0) {
     *splits = 1;
@@ -111,11 +111,12 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   split_plan(std::min<int64_t>(p->B, p->maxN), p->batch * p->Hkv, &p->sp_splits, &p->sp_len);
   split_plan(p->maxN, p->batch * p->Hkv, &p->dn_splits, &p->dn_len);
   {
-    // MLA: blocks of (split, 32 heads, sequence), about 256 in all, 64-row tiles
+    // MLA: blocks of (split, 32 heads, sequence), about 512 in all (two per
+    // CU), 32-row tiles
     const int64_t n = std::min<int64_t>(p->B, p->maxN);
-    int64_t sp = cdiv(256, (int64_t)p->batch * std::max(1, p->Hq / 32));
-    sp = std::max<int64_t>(1, std::min<int64_t>({sp, cdiv(n, 64), 64}));
-    p->ml_len = (int)(cdiv(cdiv(n, sp), 64) * 64);
+    int64_t sp = cdiv(512, (int64_t)p->batch * std::max(1, p->Hq / 32));
+    sp = std::max<int64_t>(1, std::min<int64_t>({sp, cdiv(n, 32), 64}));
+    p->ml_len = (int)(cdiv(cdiv(n, sp), 32) * 32);
     p->ml_splits = (int)cdiv(n, p->ml_len);
     mla_dense_plan(p->maxN, p->batch, p->Hq, &p->md_splits, &p->md_len);
   }

@@ -10,17 +10,21 @@
 // D[4(l/16)+j][l%16]).
 //
 // Block = (split of the selected rows, block of 32 query heads, sequence),
-// 4 wavefronts.  Per tile of 64 rows:
-//   * the rows are gathered once into LDS (row stride 584 elements);
-//   * S = Q K^T: wavefront w computes the 32 heads x 16 rows [16w, 16w+16)
-//     over 18 K-steps, Q coming from LDS;
-//   * online softmax per head (base 2): tile max and sum are combined across
-//     the four wavefronts through LDS, the running state rescales the output;
+// 4 wavefronts, two blocks per CU (about 44 KB of LDS, at most 256 registers
+// per lane).  Per tile of 32 rows:
+//   * the rows are gathered once into LDS (row stride 584 elements); the next
+//     tile's loads are in flight in registers while the current one computes;
+//   * S = Q K^T: wavefront w takes heads [16 (w & 1), +16) over the dims
+//     [288 (w >> 1), +288) (9 K-steps) for all 32 rows, so its part of Q
+//     stays in registers (9 MFMA operands) for the whole block and K comes
+//     from LDS; the two dim halves are summed through LDS, wavefront w
+//     finishing rows [16 (w >> 1), +16);
+//   * online softmax per head (base 2): the two wavefronts holding a head's
+//     rows exchange tile maxima and sums through LDS; every wavefront keeps
+//     the running state of all 32 heads and rescales its part of the output;
 //   * O += P V: wavefront w owns output dims [128w, 128w+128) (2 x 8 tiles of
-//     16x16); P comes from LDS, V is read column-wise from the same LDS tile.
-//     Within each group of 32 rows the K index g*8+i of lane group g maps to
-//     row 4i+g, so the four lane groups read rows on different LDS banks; P is
-//     stored in that order.
+//     16x16), P (bf16) comes from LDS, V is read column-wise from the same LDS
+//     tile with the transposing LDS read (4 rows of one dim per instruction).
 // The split's partial (unnormalised o, running max, running sum) goes to the
 // workspace and merge_kernel<512> combines the splits.
 //
@@ -45,12 +49,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = kMlaLatent + kMlaRope;  // 576
 constexpr int kV = kMlaLatent;             // 512
 constexpr int kHB = 32;                    // query heads per block
-constexpr int kTile = 64;                  // selected rows per tile
-constexpr int kRow = kD + 8;               // LDS row stride of K rows and Q rows (elements)
+constexpr int kTile = 32;                  // selected rows per tile
+constexpr int kRow = kD + 8;               // LDS row stride of K rows (elements)
 constexpr int kPRow = kTile + 8;           // LDS row stride of P (elements)
 constexpr int kThreads = 256;
-constexpr int kChunkRows = 1024;           // rows resolved at a time (16 tiles)
+constexpr int kChunkRows = 1024;           // rows resolved at a time (32 tiles)
 constexpr int kTilesPerChunk = kChunkRows / kTile;
+constexpr int kKSteps = kD / 32;           // 18
+constexpr int kKHalf = kKSteps / 2;        // 9 K-steps per wavefront
+constexpr int kPieces = kTile * (kD / 8) / kThreads;   // 16-byte pieces per thread per tile: 9
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -75,13 +82,13 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const uint16_t* p) {
 }  // namespace
 
 template <bool DENSE>
-__global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void mla_attend_kernel(AttendArgs a) {
   __shared__ __align__(16) uint16_t Kt[kTile * kRow];
-  __shared__ __align__(16) uint16_t Qs[kHB * kRow];
   __shared__ __align__(16) uint16_t Ps[kHB * kPRow];
-  __shared__ __align__(16) float red_m[kHB][4];   // [head][wavefront]
-  __shared__ __align__(16) float red_l[kHB][4];
-  __shared__ int rows[kChunkRows];                // physical rows of the current chunk of tiles
+  __shared__ __align__(16) float red_m[2][kHB];     // [row half][head] tile maxima
+  __shared__ __align__(16) float red_l[2][kHB];     // [row half][head] tile sums
+  __shared__ int rows[kChunkRows];                  // physical rows of the current chunk of tiles
+  __shared__ f32x4 Sx[4][64];                       // [heads half][row half][lane] S halves in exchange
 
   const int HB = a.Hq / kHB;
   const int L = (int)blockIdx.x;
@@ -91,6 +98,8 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
   const int s = u % a.splits, b = u / a.splits;
   const int tid = (int)threadIdx.x, l = lane_id(), w = tid >> 6;
   const int g = l >> 4, c = l & 15;
+  const int mt = w & 1, rt = w >> 1;             // S: heads 16 mt .., rows 16 rt .. of the tile
+  const int kh = rt;                             // and dims [288 kh, +288) of the product
   int N = a.seq_lens[b];
   const int cap = a.max_pages * a.P;
   N = N < 0 ? 0 : (N > cap ? cap : N);
@@ -121,17 +130,16 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
     for (int j = 0; j < kChunkRows / kThreads; ++j)
       rows[tid + j * kThreads] = tv[j] >= 0 ? pv[j] * a.P + tv[j] % a.P : -1;
   };
-  // the tile's 64 x 72 16-byte pieces: 18 per thread, all loads in flight together
-  constexpr int kPieces = kTile * (kD / 8) / kThreads;   // 18
-  // (row indices read first, loads unconditional at row max(r, 0); pieces of
-  // missing rows are zeroed when stored, from the bit mask `miss`; `vld`
-  // records whether this lane's row w*16 + c of the tile exists)
+  // the tile's 32 x 72 16-byte pieces, 9 per thread, all loads in flight
+  // together (row indices read first, loads unconditional at row max(r, 0);
+  // pieces of missing rows are zeroed when stored, from the bit mask `miss`;
+  // `vld` records whether this lane's S row 16 rt + c of the tile exists)
   auto fetch = [&](int kt, uint4 (&reg)[kPieces], uint32_t& miss, bool& vld) {
     const int* rw = rows + (kt % kTilesPerChunk) * kTile;
     int rr[kPieces];
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) rr[k] = rw[(tid + k * kThreads) / (kD / 8)];
-    vld = rw[w * 16 + c] >= 0;
+    vld = rw[rt * 16 + c] >= 0;
     miss = 0u;
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
@@ -148,41 +156,35 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
     }
   };
 
-  // Q of the 32 heads into LDS (9 pieces per thread, loads together, in
-  // flight while the first chunk's rows are resolved)
+  // this wavefront's 16 heads of Q over its half of the 576 dims as MFMA A
+  // operands (lane: head 16 mt + c, dims (9 kh + ks) * 32 + 8 g .. + 8),
+  // loaded while the first chunk's rows resolve
+  bf16x8 qa[kKHalf];
   {
-    constexpr int kQ = kHB * (kD / 8) / kThreads;        // 9
-    uint4 qv[kQ];
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + hb * kHB + mt * 16 + c) * kD + kh * kKHalf * 32 + g * 8;
 #pragma unroll
-    for (int k = 0; k < kQ; ++k) {
-      const int q = tid + k * kThreads, m = q / (kD / 8), cc = q % (kD / 8);
-      qv[k] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + hb * kHB + m) * kD + cc * 8);
-    }
-    fill_chunk(0);
-#pragma unroll
-    for (int k = 0; k < kQ; ++k) {
-      const int q = tid + k * kThreads, m = q / (kD / 8), cc = q % (kD / 8);
-      *reinterpret_cast<uint4*>(&Qs[m * kRow + cc * 8]) = qv[k];
-    }
+    for (int ks = 0; ks < kKHalf; ++ks) qa[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32);
   }
+  fill_chunk(0);
   __syncthreads();
   uint4 reg[kPieces];
   uint32_t miss;
   bool vnext;
   fetch(0, reg, miss, vnext);
 
-  // lane state: heads mt*16 + 4g + j (mt = 0, 1; j = 0..3)
+  // running state of heads mt' * 16 + 4 g + j (mt' = 0, 1; j = 0..3): the
+  // rows of this lane's output accumulators
   float m_run[2][4], l_run[2][4];
   f32x4 O[2][8];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int m2 = 0; m2 < 2; ++m2) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      m_run[mt][j] = -INFINITY;
-      l_run[mt][j] = 0.0f;
+      m_run[m2][j] = -INFINITY;
+      l_run[m2][j] = 0.0f;
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) O[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nt = 0; nt < 8; ++nt) O[m2][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   for (int k = 0; k < n_tiles; ++k) {
@@ -193,103 +195,101 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(AttendArgs a) {
     __syncthreads();
     if (k + 1 < n_tiles) fetch(k + 1, reg, miss, vnext);     // next tile's loads overlap this tile's math
 
-    // ---- S = Q K^T for rows [16w, 16w + 16)
-    f32x4 S[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+    // ---- S = Q K^T over this wavefront's half of the dims for both row
+    // halves of the tile (heads 16 mt + 4 g + j, rows 16 t + c); the half of
+    // the other wavefront's row half goes to it through LDS
+    f32x4 S0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
 #pragma unroll
-    for (int k0 = 0; k0 < kD / 32; k0 += 6) {        // operands of 6 K-steps read together
-      bf16x8 bk[6], aq[2][6];
+    for (int k0 = 0; k0 < kKHalf; k0 += 3) {         // K operands of 3 K-steps read together
+      bf16x8 b0[3], b1[3];
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        const int kc = (k0 + i) * 32 + g * 8;
-        bk[i] = *reinterpret_cast<const bf16x8*>(&Kt[(w * 16 + c) * kRow + kc]);
-        aq[0][i] = *reinterpret_cast<const bf16x8*>(&Qs[c * kRow + kc]);
-        aq[1][i] = *reinterpret_cast<const bf16x8*>(&Qs[(16 + c) * kRow + kc]);
+      for (int i = 0; i < 3; ++i) {
+        const int col = (kh * kKHalf + k0 + i) * 32 + g * 8;
+        b0[i] = *reinterpret_cast<const bf16x8*>(&Kt[c * kRow + col]);
+        b1[i] = *reinterpret_cast<const bf16x8*>(&Kt[(16 + c) * kRow + col]);
       }
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        S[0] = mfma16(aq[0][i], bk[i], S[0]);
-        S[1] = mfma16(aq[1][i], bk[i], S[1]);
+      for (int i = 0; i < 3; ++i) {
+        S0 = mfma16(qa[k0 + i], b0[i], S0);
+        S1 = mfma16(qa[k0 + i], b1[i], S1);
       }
     }
-    float x[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[mt][j] = valid ? S[mt][j] * a.sm_log2 : -INFINITY;
-        const float tm = row16_max(x[mt][j]);
-        if (c == 0) red_m[mt * 16 + g * 4 + j][w] = tm;
-      }
+    Sx[mt * 2 + (rt ^ 1)][l] = rt == 0 ? S1 : S0;
     __syncthreads();
-    // ---- softmax update (every wavefront computes the same state)
-    const int kpos = w * 16 + c;                       // P in natural row order
-    float4 rm[2][4];
+    const f32x4 S = (rt == 0 ? S0 : S1) + Sx[mt * 2 + rt][l];
+    float x[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int j = 0; j < 4; ++j) {
+      x[j] = valid ? S[j] * a.sm_log2 : -INFINITY;
+      const float tm = row16_max(x[j]);
+      if (c == 0) red_m[rt][mt * 16 + g * 4 + j] = tm;
+    }
+    __syncthreads();
+    // ---- new running max of every head this lane accumulates (both halves of
+    // the tile); the state and this lane's output rows are rescaled at once
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rm[mt][j] = *reinterpret_cast<const float4*>(red_m[mt * 16 + g * 4 + j]);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int hh = mt * 16 + g * 4 + j;
-        const float tm = fmaxf(fmaxf(rm[mt][j].x, rm[mt][j].y), fmaxf(rm[mt][j].z, rm[mt][j].w));
-        const float mn = fmaxf(m_run[mt][j], tm);
+        const int hh = m2 * 16 + g * 4 + j;
+        const float mn = fmaxf(m_run[m2][j], fmaxf(red_m[0][hh], red_m[1][hh]));
         const float ms = (mn == -INFINITY) ? 0.0f : mn;
-        const float al = __builtin_amdgcn_exp2f(m_run[mt][j] - ms);
-        const float p = __builtin_amdgcn_exp2f(x[mt][j] - ms);
-        const float ps = row16_sum(p);
-        if (c == 0) red_l[hh][w] = ps;
-        l_run[mt][j] *= al;
-        m_run[mt][j] = mn;
+        const float al = __builtin_amdgcn_exp2f(m_run[m2][j] - ms);
+        m_run[m2][j] = mn;
+        l_run[m2][j] *= al;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) O[mt][nt][j] *= al;
-        Ps[hh * kPRow + kpos] = __builtin_bit_cast(uint16_t, (__bf16)p);
+        for (int nt = 0; nt < 8; ++nt) O[m2][nt][j] *= al;
       }
+    // ---- P of this wavefront's (16 heads x 16 rows), its row sums
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hh = mt * 16 + g * 4 + j;
+      const float mn = mt == 0 ? m_run[0][j] : m_run[1][j];
+      const float ms = (mn == -INFINITY) ? 0.0f : mn;
+      const float p = __builtin_amdgcn_exp2f(x[j] - ms);
+      const float ps = row16_sum(p);
+      if (c == 0) red_l[rt][hh] = ps;
+      Ps[hh * kPRow + rt * 16 + c] = __builtin_bit_cast(uint16_t, (__bf16)p);
+    }
     __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 rl = *reinterpret_cast<const float4*>(red_l[mt * 16 + g * 4 + j]);
-        l_run[mt][j] += (rl.x + rl.y) + (rl.z + rl.w);
+        const int hh = m2 * 16 + g * 4 + j;
+        l_run[m2][j] += red_l[0][hh] + red_l[1][hh];
       }
 
-    // ---- O += P V for output dims [128w, 128w + 128)
+    // ---- O += P V for output dims [128w, 128w + 128): one K-step of 32 rows
+    bf16x8 ap[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 ap[2];
+    for (int m2 = 0; m2 < 2; ++m2) ap[m2] = *reinterpret_cast<const bf16x8*>(&Ps[(m2 * 16 + c) * kPRow + g * 8]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        ap[mt] = *reinterpret_cast<const bf16x8*>(&Ps[(mt * 16 + c) * kPRow + kk * 32 + g * 8]);
+    for (int nt = 0; nt < 8; ++nt) {
+      // B operand: rows 8g .. 8g+7 of dim w*128 + nt*16 + c, two transposing
+      // reads of 4 rows each (lane 4k + a of the group points at row +k, dims +4a ..)
+      const int dim0 = w * 128 + nt * 16 + (c & 3) * 4;
+      const int row0 = g * 8 + (c >> 2);
+      const bf16x4 v0 = ds_read_tr(&Kt[row0 * kRow + dim0]);
+      const bf16x4 v1 = ds_read_tr(&Kt[(row0 + 4) * kRow + dim0]);
+      const bf16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        // B operand: rows kk*32 + 8g .. +7 of output dim w*128 + nt*16 + c, two
-        // transposing reads of 4 rows each (lane 4k + a of the group points at
-        // row +k, dims +4a .. +4a+3)
-        const int dim0 = w * 128 + nt * 16 + (c & 3) * 4;
-        const int row0 = kk * 32 + g * 8 + (c >> 2);
-        const bf16x4 v0 = ds_read_tr(&Kt[row0 * kRow + dim0]);
-        const bf16x4 v1 = ds_read_tr(&Kt[(row0 + 4) * kRow + dim0]);
-        const bf16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) O[mt][nt] = mfma16(ap[mt], bv, O[mt][nt]);
-      }
+      for (int m2 = 0; m2 < 2; ++m2) O[m2][nt] = mfma16(ap[m2], bv, O[m2][nt]);
     }
   }
 
   // ---- this split's partial
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int head = hb * kHB + mt * 16 + g * 4 + j;
+      const int head = hb * kHB + m2 * 16 + g * 4 + j;
       const int64_t pj = ((int64_t)b * a.Hq + head) * a.splits + s;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) a.part_o[pj * kV + w * 128 + nt * 16 + c] = O[mt][nt][j];
+      for (int nt = 0; nt < 8; ++nt) a.part_o[pj * kV + w * 128 + nt * 16 + c] = O[m2][nt][j];
       if (w == 0 && c == 0) {
-        a.part_ml[pj * 2] = m_run[mt][j];
-        a.part_ml[pj * 2 + 1] = l_run[mt][j];
+        a.part_ml[pj * 2] = m_run[m2][j];
+        a.part_ml[pj * 2 + 1] = l_run[m2][j];
       }
     }
 }
