@@ -45,6 +45,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = kMlaLatent + kMlaRope;  // 576
 constexpr int kV = kMlaLatent;             // 512
@@ -115,44 +116,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
   // physical rows (-1: none) of the chunk of tiles ch into rows[]: every
-  // thread resolves 4 positions, index and block-table loads batched
+  // thread resolves 4 positions, index and block-table loads batched and
+  // unconditional (clamped to the split's last position and to page 0), so
+  // that no load sits behind a branch
   auto fill_chunk = [&](int ch) {
     const int base = i0 + ch * kChunkRows;
     int tv[kChunkRows / kThreads], pv[kChunkRows / kThreads];
 #pragma unroll
     for (int j = 0; j < kChunkRows / kThreads; ++j) {
       const int ii = base + tid + j * kThreads;
-      tv[j] = ii < i1 ? (DENSE ? lo + ii : idx[ii]) : -1;
+      tv[j] = DENSE ? lo + ii : idx[ii < i1 ? ii : i1 - 1];
+      if (ii >= i1) tv[j] = -1;
     }
 #pragma unroll
-    for (int j = 0; j < kChunkRows / kThreads; ++j) pv[j] = tv[j] >= 0 ? bt[tv[j] / a.P] : 0;
+    for (int j = 0; j < kChunkRows / kThreads; ++j) pv[j] = bt[(tv[j] < 0 ? 0 : tv[j]) / a.P];
 #pragma unroll
     for (int j = 0; j < kChunkRows / kThreads; ++j)
       rows[tid + j * kThreads] = tv[j] >= 0 ? pv[j] * a.P + tv[j] % a.P : -1;
   };
   // the tile's 32 x 72 16-byte pieces, 9 per thread, all loads in flight
-  // together (row indices read first, loads unconditional at row max(r, 0);
-  // pieces of missing rows are zeroed when stored, from the bit mask `miss`;
-  // `vld` records whether this lane's S row 16 rt + c of the tile exists)
-  auto fetch = [&](int kt, uint4 (&reg)[kPieces], uint32_t& miss, bool& vld) {
+  // together.  A missing row (past the split's end) is loaded from the tile's
+  // first row, which always exists: its logits are masked to -inf, so its
+  // weight is 0 and its (finite) values add nothing.  `vld` records whether
+  // this lane's S row 16 rt + c of the tile exists.
+  auto fetch = [&](int kt, u32x4 (&reg)[kPieces], bool& vld) {
     const int* rw = rows + (kt % kTilesPerChunk) * kTile;
+    const int r0 = rw[0];
     int rr[kPieces];
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) rr[k] = rw[(tid + k * kThreads) / (kD / 8)];
     vld = rw[rt * 16 + c] >= 0;
-    miss = 0u;
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
       const int cc = (tid + k * kThreads) % (kD / 8);
-      miss |= (rr[k] < 0 ? 1u : 0u) << k;
-      reg[k] = *reinterpret_cast<const uint4*>(a.k_cache + (int64_t)(rr[k] < 0 ? 0 : rr[k]) * kD + cc * 8);
+      reg[k] = *reinterpret_cast<const u32x4*>(a.k_cache + (int64_t)(rr[k] < 0 ? r0 : rr[k]) * kD + cc * 8);
     }
   };
-  auto put = [&](const uint4 (&reg)[kPieces], uint32_t miss) {
+  auto put = [&](const u32x4 (&reg)[kPieces]) {
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
       const int q = tid + k * kThreads, tt = q / (kD / 8), cc = q % (kD / 8);
-      *reinterpret_cast<uint4*>(&Kt[tt * kRow + cc * 8]) = ((miss >> k) & 1u) ? make_uint4(0, 0, 0, 0) : reg[k];
+      *reinterpret_cast<u32x4*>(&Kt[tt * kRow + cc * 8]) = reg[k];
     }
   };
 
@@ -167,10 +171,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   fill_chunk(0);
   __syncthreads();
-  uint4 reg[kPieces];
-  uint32_t miss;
+  u32x4 reg[kPieces];
   bool vnext;
-  fetch(0, reg, miss, vnext);
+  fetch(0, reg, vnext);
 
   // running state of heads mt' * 16 + 4 g + j (mt' = 0, 1; j = 0..3): the
   // rows of this lane's output accumulators
@@ -189,11 +192,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   for (int k = 0; k < n_tiles; ++k) {
     __syncthreads();                                   // previous tile consumed
-    put(reg, miss);
+    put(reg);
     const bool valid = vnext;
     if (k + 1 < n_tiles && (k + 1) % kTilesPerChunk == 0) fill_chunk((k + 1) / kTilesPerChunk);
     __syncthreads();
-    if (k + 1 < n_tiles) fetch(k + 1, reg, miss, vnext);     // next tile's loads overlap this tile's math
+    // next tile's loads overlap this tile's math (the last tile fetches itself
+    // again, so that the loads are unconditional and need no register copies)
+    fetch(k + 1 < n_tiles ? k + 1 : k, reg, vnext);
 
     // ---- S = Q K^T over this wavefront's half of the dims for both row
     // halves of the tile (heads 16 mt + 4 g + j, rows 16 t + c); the half of
@@ -214,9 +219,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         S1 = mfma16(qa[k0 + i], b1[i], S1);
       }
     }
-    Sx[mt * 2 + (rt ^ 1)][l] = rt == 0 ? S1 : S0;
+    f32x4 S, So;                                       // own and other row half (element selects)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      S[i] = rt == 0 ? S0[i] : S1[i];
+      So[i] = rt == 0 ? S1[i] : S0[i];
+    }
+    Sx[mt * 2 + (rt ^ 1)][l] = So;
     __syncthreads();
-    const f32x4 S = (rt == 0 ? S0 : S1) + Sx[mt * 2 + rt][l];
+    S += Sx[mt * 2 + rt][l];
     float x[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -227,6 +238,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __syncthreads();
     // ---- new running max of every head this lane accumulates (both halves of
     // the tile); the state and this lane's output rows are rescaled at once
+    float m_own[4];                                    // new maxima of heads 16 mt + 4 g + j
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
@@ -237,6 +249,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const float al = __builtin_amdgcn_exp2f(m_run[m2][j] - ms);
         m_run[m2][j] = mn;
         l_run[m2][j] *= al;
+        if (m2 == 0) m_own[j] = ms;
+        else m_own[j] = mt == 0 ? m_own[j] : ms;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) O[m2][nt][j] *= al;
       }
@@ -244,8 +258,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int hh = mt * 16 + g * 4 + j;
-      const float mn = mt == 0 ? m_run[0][j] : m_run[1][j];
-      const float ms = (mn == -INFINITY) ? 0.0f : mn;
+      const float ms = m_own[j];
       const float p = __builtin_amdgcn_exp2f(x[j] - ms);
       const float ps = row16_sum(p);
       if (c == 0) red_l[rt][hh] = ps;
