@@ -46,16 +46,17 @@ void split_plan(int64_t n_tok_max, int pairs, int* splits, int* len) {
   *splits = (int)cdiv(n_tok_max, l);
 }
 
-// MLA dense split plan: about 512 blocks of (split, 32 heads, sequence), at
-// most 256 splits (the merge holds one split per thread), 64-row multiples.
+// MLA dense split plan: about 512 blocks of (split, 64 heads, sequence) (two
+// per CU), at least 128 rows per split, at most 256 splits (the merge holds
+// one split per thread), 64-row multiples.
 void mla_dense_plan(int64_t n, int batch, int Hq, int* splits, int* len) {
   if (n <= 0) {
     *splits = 1;
     *len = 64;
     return;
   }
-  int64_t sp = cdiv(512, (int64_t)batch * std::max(1, Hq / 32));
-  sp = std::max<int64_t>(1, std::min<int64_t>({sp, cdiv(n, 64), 256}));
+  int64_t sp = cdiv(512, (int64_t)batch * cdiv(Hq, 64));
+  sp = std::max<int64_t>(1, std::min<int64_t>({sp, cdiv(n, 128), 256}));
   *len = (int)(cdiv(cdiv(n, sp), 64) * 64);
   *splits = (int)cdiv(n, *len);
 }
