@@ -227,6 +227,19 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
       if (j < hg) qv[j] = *reinterpret_cast<const uint4*>(qp + (int64_t)j * din);
   }
 
+  // this thread's rows of M for qhat (8 threads per output, float4 groups
+  // part, part + 8, ...): loaded now, beside the query, when they are at most
+  // 4 groups (d = 128), so that qhat does not wait for them later
+  const int mo = tid >> 3, mpart = tid & 7;
+  const int nf = dm / 32;                      // float4 groups per thread: 4, 8 or 16
+  const bool mpre = nf <= 4 && mo < a.r;
+  float4 mpv[4];
+  if (mpre) {
+    const float* m = Mh + (int64_t)mo * dm + mpart * 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mpv[k] = k < nf ? *reinterpret_cast<const float4*>(m + k * 32) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
   // sample plan: a strided set of whole pages; tau will be the ks-th largest
   // sampled key with ks / sample = target / N, target = min(2B, cap/2)
   const bool sampled = !a.force_exact && N > kCandCap;
@@ -243,13 +256,13 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   const int ns = sp * a.P;
   // sample loads go out in two steps around the query work: the block-table
   // entries of every round first (with the query loads), then each round's
-  // FP8 rows (round 0 before the projection).  Round r covers the sample
-  // indices u = (r TPT + j) threads + tid, j < TPT.
+  // FP8 rows (round 0 as soon as the query is summed).  Round r covers the
+  // sample indices u = (r TPT + j) threads + tid, j < TPT.
   uint4 pc[TPT][R];
   float sc[TPT];
-  if (sampled) {                               // all loads first, then the LDS stores
-    constexpr int KS = kSampleMax / kPrologueThreads;
-    int ph[KS];
+  constexpr int KS = kSampleMax / kPrologueThreads;
+  int ph[KS];
+  if (sampled) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       const int u = k * kPrologueThreads + tid;
@@ -259,9 +272,6 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
         if (pl * a.P + u % a.P < N) ph[k] = a.block_table[(int64_t)b * a.max_pages + pl];
       }
     }
-#pragma unroll
-    for (int k = 0; k < KS; ++k)               // each thread reads back only its own entries
-      if (k * kPrologueThreads + tid < ns) sph[k * kPrologueThreads + tid] = ph[k];
   }
   auto issue_rows = [&](int r) {
 #pragma unroll
@@ -291,13 +301,20 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 #pragma unroll
     for (int k = 0; k < 8; ++k) qpart[qgrp * din + qc * 8 + k] = acc[k];
   }
+  // the query registers are free now: the sample pages go to LDS and round
+  // 0's FP8 rows go out (each thread reads back only its own sph entries)
+  if (sampled) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      if (k * kPrologueThreads + tid < ns) sph[k * kPrologueThreads + tid] = ph[k];
+    issue_rows(0);
+  }
   __syncthreads();
   for (int i = tid; i < din; i += kPrologueThreads) {
     double acc = 0.0;
     for (int g = 0; g < groups; ++g) acc += qpart[g * din + i];
     qbar[i] = acc / (double)a.G;
   }
-  if (sampled) issue_rows(0);
   // the new token of this sequence (jssa_decode): projected exactly as
   // jssa_store does (eight threads per output, project_part / proj_combine)
   const int new_slot = a.k_new ? a.slot_new[b] : -1;
@@ -316,10 +333,21 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   // ... (the 8 threads of an output read 128 contiguous bytes per step), partial
   // sums added in a fixed xor order
   {
-    const int o = tid >> 3, part = tid & 7;
+    const int o = mo, part = mpart;
     double v = 0.0;
-    if (o < a.r) {
-      const int nf = dm / 32;                 // float4 groups per thread: 4, 8 or 16
+    if (mpre) {
+      const double* qb = qbar + part * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k < nf) {
+          const double* qq = qb + k * 32;
+          v = __builtin_fma((double)mpv[k].x, qq[0], v);
+          v = __builtin_fma((double)mpv[k].y, qq[1], v);
+          v = __builtin_fma((double)mpv[k].z, qq[2], v);
+          v = __builtin_fma((double)mpv[k].w, qq[3], v);
+        }
+      }
+    } else if (o < a.r) {
       const float* m = Mh + (int64_t)o * dm + part * 4;
       const double* qb = qbar + part * 4;
       for (int k0 = 0; k0 < nf; k0 += 8) {     // 8 loads in flight per batch
