@@ -49,14 +49,23 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // Combine the splits of every (sequence, query head): o = sum_s 2^(m_s - m*) o_s /
 // sum_s 2^(m_s - m*) l_s, lse = ln 2 * (m* + log2 sum_s 2^(m_s - m*) l_s).
-// One block per (query head, sequence); the (m_s, l_s) of all splits are read
-// once into LDS, then every thread combines its dims.
+// One block per (query head, sequence).  Every load goes out first: thread s
+// reads split s's (m_s, l_s), and each thread requests its share of the
+// partial outputs (for D < 256 the block splits into 256 / D groups that take
+// interleaved splits of every dim; for D >= 256 a thread takes D / 256 dims
+// of every split), up to 16 splits at once, clamped to the last split that
+// exists.  The block max and the weights 2^(m_s - m*) are formed while those
+// loads are in flight (two barriers), then the products are summed (groups
+// added through LDS with a third barrier).
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(AttendArgs a) {
+  constexpr int SG = D >= 256 ? 1 : 256 / D;   // thread groups over the splits
+  constexpr int DPT = D >= 256 ? D / 256 : 1;  // dims per thread
+  constexpr int MB = 16;                       // splits per thread per batch of loads
   __shared__ float wsplit[256];
-  __shared__ float lsum;
-  __shared__ float mmax;
-  const int j = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
+  __shared__ float wred[2][4];
+  __shared__ float gpart[SG > 1 ? (SG - 1) * D : 1];
+  const int j = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x, lane = lane_id(), w = tid >> 6;
   int N = a.seq_lens[b];
   const int cap = a.max_pages * a.P;
   N = N < 0 ? 0 : (N > cap ? cap : N);
@@ -64,42 +73,70 @@ __global__ __launch_bounds__(256) void merge_kernel(AttendArgs a) {
   if (a.indices) n_tok = N < a.B ? N : a.B;
   else n_tok = (a.window > 0 && N > a.window) ? a.window : N;
   // partials of the splits that hold positions (a.parts per split: one per
-  // wavefront for the GQA kernel, one per block for the MLA kernel)
+  // wavefront for the GQA kernel, one per block for the MLA kernels)
   const int ns = min(a.splits, (n_tok + a.split_len - 1) / a.split_len) * a.parts;
   const int64_t pj0 = ((int64_t)b * a.Hq + j) * ((int64_t)a.splits * a.parts);
-  // at most 256 partials: thread s holds partial s
-  float ms_ = -INFINITY, ls_ = 0.0f;
-  if (tid < ns) {
-    ls_ = a.part_ml[(pj0 + tid) * 2 + 1];
-    ms_ = ls_ > 0.0f ? a.part_ml[(pj0 + tid) * 2] : -INFINITY;
+  uint16_t* orow = a.out + ((int64_t)b * a.Hq + j) * D;
+  if (ns <= 0) {                               // no positions: zeros
+    for (int d = tid; d < D; d += 256) orow[d] = 0;
+    if (tid == 0 && a.lse_out) a.lse_out[(int64_t)b * a.Hq + j] = -INFINITY;
+    return;
   }
-  float mm = wave_max(ms_);
-  if ((tid & 63) == 0) wsplit[tid >> 6] = mm;
-  __syncthreads();
-  if (tid == 0) {
-    float m4 = -INFINITY;
-    for (int i = 0; i < 4; ++i) m4 = fmaxf(m4, wsplit[i]);
-    mmax = m4;
-  }
-  __syncthreads();
-  mm = mmax;
-  const float msafe = (mm == -INFINITY) ? 0.0f : mm;
-  const float f = (tid < ns && ls_ > 0.0f) ? __builtin_amdgcn_exp2f(ms_ - msafe) : 0.0f;
-  __syncthreads();
-  wsplit[tid] = f;
-  float lw = ls_ * f;
+  const int g = SG > 1 ? tid / D : 0;
+  const int d0 = SG > 1 ? tid % D : tid;
+  const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (pj0 + (tid < ns ? tid : ns - 1)) * 2);
+  float pv[MB][DPT];
+  auto fetch = [&](int b0) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o);
-  if (tid == 0) lsum = 0.0f;
+    for (int i = 0; i < MB; ++i) {
+      const int sp = g + (b0 + i) * SG;
+      const float* src = a.part_o + (pj0 + (sp < ns ? sp : ns - 1)) * D + d0;
+#pragma unroll
+      for (int k = 0; k < DPT; ++k) pv[i][k] = src[k * 256];
+    }
+  };
+  fetch(0);
+
+  const float ms = (tid < ns && ml.y > 0.0f) ? ml.x : -INFINITY;
+  const float ls = tid < ns ? ml.y : 0.0f;
+  const float wm = wave_max(ms);
+  if (lane == 0) wred[0][w] = wm;
   __syncthreads();
-  if ((tid & 63) == 0) atomicAdd(&lsum, lw);
+  const float mm = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+  const float msafe = (mm == -INFINITY) ? 0.0f : mm;
+  const float f = (tid < ns && ls > 0.0f) ? __builtin_amdgcn_exp2f(ms - msafe) : 0.0f;
+  wsplit[tid] = f;
+  const float lw = wave_sum(ls * f);
+  if (lane == 0) wred[1][w] = lw;
   __syncthreads();
-  const float L = lsum;
+  const float L = (wred[1][0] + wred[1][1]) + (wred[1][2] + wred[1][3]);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  for (int dim = tid; dim < D; dim += 256) {
-    float acc = 0.0f;
-    for (int s = 0; s < ns; ++s) acc += a.part_o[(pj0 + s) * D + dim] * wsplit[s];
-    a.out[((int64_t)b * a.Hq + j) * D + dim] = f32_to_bf16(acc * inv);
+
+  float acc[DPT];
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) acc[k] = 0.0f;
+  const int mine = (ns - g + SG - 1) / SG;     // splits g, g + SG, ... below ns
+  for (int b0 = 0; b0 < mine; b0 += MB) {
+    if (b0 > 0) fetch(b0);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int sp = g + (b0 + i) * SG;
+      const float wt = sp < ns ? wsplit[sp] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < DPT; ++k) acc[k] = __builtin_fmaf(pv[i][k], wt, acc[k]);
+    }
+  }
+  if (SG > 1) {
+    if (g > 0) gpart[(g - 1) * D + d0] = acc[0];
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+      for (int q = 1; q < SG; ++q) acc[0] += gpart[(q - 1) * D + d0];
+      orow[d0] = f32_to_bf16(acc[0] * inv);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) orow[d0 + k * 256] = f32_to_bf16(acc[k] * inv);
   }
   if (tid == 0 && a.lse_out) a.lse_out[(int64_t)b * a.Hq + j] = L > 0.0f ? (mm + log2f(L)) * kLn2 : -INFINITY;
 }
