@@ -271,9 +271,13 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
         float pp[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) pp[g] = row_bcast_f(p[g], u0 + u);
+        // a missing position's row is read from slot 0: its weight is 0, and
+        // its values are zeroed so that whatever slot 0 holds adds nothing
+        const bool ok = row_bcast(ri, u0 + u) >= 0;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const uint32_t ww[4] = {vr[u][v].x, vr[u][v].y, vr[u][v].z, vr[u][v].w};
+          const uint4 vv = vr[u][v];
+          const uint32_t ww[4] = {ok ? vv.x : 0u, ok ? vv.y : 0u, ok ? vv.z : 0u, ok ? vv.w : 0u};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float v0 = bf16_lo(ww[e]), v1 = bf16_hi(ww[e]);

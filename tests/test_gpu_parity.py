@@ -709,3 +709,74 @@ def test_gather_attend_parity_mla():
         o, l = omla.attend(q[b], rows[b][idx[b, 0][idx[b, 0] >= 0]], w.sm_scale)
         check_attention(got[b], o)
         assert np.all(np.abs(glse[b] - l) <= 1e-3)
+
+
+def _nan_first_page(cache, bt):
+    """The cache with one NaN page in front and the block table moved past it: physical slot 0 then
+    belongs to no sequence and holds NaN."""
+    pad = torch.full((1,) + tuple(cache.shape[1:]), float("nan"), dtype=cache.dtype)
+    return torch.cat([pad, cache]), bt + 1
+
+
+def test_nan_in_unused_slot_zero_does_not_reach_the_output():
+    """A partial batch (past a sequence's end) reads its missing positions at slot 0 with weight 0;
+    whatever slot 0 holds must add nothing: indexed, dense, windowed and gathered, GQA and MLA."""
+    w, case, m32, rows_k, rows_v, stored = _gqa("short_ctx")
+    lay = case.layers[0]
+    kc, bt = _nan_first_page(lay.k_cache, case.block_table)
+    vc, _ = _nan_first_page(lay.v_cache, case.block_table)
+    q = bf16_bits(lay.q)
+    idx = np.full((w.batch, w.num_kv_heads, w.budget), -1, np.int32)
+    for b in range(w.batch):
+        qhat = ogqa.project_query(q[b], m32, w.group)
+        for h in range(w.num_kv_heads):
+            s = ogqa.scores(qhat[h], stored[b][0][:, h], stored[b][1][:, h])
+            idx[b, h], _ = ogqa.select_topb(s, w.budget)
+    shape = L.shape_for(w)
+    ws = L.alloc_workspace(shape)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    qd, kd, vd, btd, sld = lay.q.to(DEV), kc.to(DEV), vc.to(DEV), bt.to(DEV), case.seq_lens.to(DEV)
+    idxd = torch.from_numpy(idx).to(DEV)
+
+    def check(sets):
+        got = out.float().cpu().numpy()
+        assert np.isfinite(got).all()
+        for b in range(w.batch):
+            for h in range(w.num_kv_heads):
+                j0 = h * w.group
+                o, _ = ogqa.attend_group(q[b, j0:j0 + w.group], rows_k[b][:, h], rows_v[b][:, h], sets(b, h),
+                                         w.sm_scale)
+                check_attention(got[b, j0:j0 + w.group], o)
+
+    L.jssa_attend(shape, qd, kd, vd, btd, sld, idxd, w.sm_scale, out, ws)
+    check(lambda b, h: idx[b, h])
+    L.jssa_gather_attend(shape, qd, kd, vd, btd, sld, idxd, w.sm_scale, out, ws)
+    check(lambda b, h: idx[b, h])
+    for window in (0, 100):
+        L.jssa_full_decode(shape, qd, kd, vd, btd, sld, window, w.sm_scale, out, ws)
+        check(lambda b, h: ogqa.window_indices(int(case.seq_lens[b]), window))
+
+    w, case, m32, rows, stored = _mla("tiny_mla")
+    lat, bt = _nan_first_page(case.latent, case.block_table)
+    q = bf16_bits(case.q)
+    idx = np.full((w.batch, 1, w.budget), -1, np.int32)
+    for b in range(w.batch):
+        s = ogqa.scores(omla.project_query(q[b], m32), stored[b][0], stored[b][1])
+        idx[b, 0], _ = ogqa.select_topb(s, w.budget)
+    shape = L.shape_for(w)
+    ws = L.alloc_workspace(shape)
+    out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+    qd, ld, btd, sld = case.q.to(DEV), lat.to(DEV), bt.to(DEV), case.seq_lens.to(DEV)
+
+    def check_mla(sets):
+        got = out.float().cpu().numpy()
+        assert np.isfinite(got).all()
+        for b in range(w.batch):
+            o, _ = omla.attend(q[b], rows[b][sets(b)], w.sm_scale)
+            check_attention(got[b], o)
+
+    L.jssa_attend(shape, qd, ld, None, btd, sld, torch.from_numpy(idx).to(DEV), w.sm_scale, out, ws)
+    check_mla(lambda b: idx[b, 0][idx[b, 0] >= 0])
+    for window in (0, 100):
+        L.jssa_full_decode(shape, qd, ld, None, btd, sld, window, w.sm_scale, out, ws)
+        check_mla(lambda b: ogqa.window_indices(int(case.seq_lens[b]), window))
