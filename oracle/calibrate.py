@@ -27,6 +27,25 @@ def bf16_to_f64(u16: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bit patterns (uint16), round to nearest, ties to even, in one step.
+
+    bf16 keeps 8 significant bits of the fp64 value: the 45 low bits of the fp64
+    significand are rounded away (ties to the even bit 45), then the result, now
+    exactly representable in fp32, gives its top 16 bits.  Valid for the normal
+    bf16 range (|x| >= 2^-126) and zero; larger magnitudes than bf16's maximum
+    and subnormal results do not occur for projected keys and are rejected."""
+    x = np.asarray(x, dtype=np.float64)
+    bits = x.view(np.uint64)
+    lsb = (bits >> np.uint64(45)) & np.uint64(1)
+    rounded = (bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
+    r = rounded.view(np.float64)
+    a = np.abs(r)
+    if np.any((a != 0) & ((a < 2.0 ** -126) | ~np.isfinite(a) | (a > 3.3895313892515355e38))):
+        raise ValueError("f64_to_bf16: value outside the normal bf16 range")
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 def group_mean(q: np.ndarray, group: int) -> np.ndarray:
     """q [..., Hq, d] -> mean over each contiguous group of G query heads [..., Hq/G, d]
     (summary page, Theoretical Foundation: the mean query of the heads of a KV head)."""

@@ -18,7 +18,9 @@ Readings where the pages are silent (each listed in the design doc):
   * scoring-cache variants (README §4 "Notes": r bytes per token and KV head):
     "e8m0" stores the scale as one byte E with value 2^(E-127), E - 127 =
     ceil(log2 of the fp32 scale above), codes of y_i / 2^(E-127); "none"
-    stores no scale, codes of y_i themselves (saturating);
+    stores no scale, codes of y_i themselves (saturating); "bf16" is the
+    README's non-FP8 option (jssa_fp8_projk off: BF16 projected keys), y_i
+    rounded to bf16, 2 bytes per element, no scale;
   * the score is scale * sum_i qhat_i dec(code_i) and -0 counts as +0;
   * order by (score descending, position ascending): on a tie at the B-th score
     the lowest position wins; output positions ascending, padded with -1;
@@ -33,7 +35,7 @@ from typing import Tuple
 import numpy as np
 
 from . import fp8
-from .calibrate import bf16_to_f64, group_mean
+from .calibrate import bf16_to_f64, f64_to_bf16, group_mean
 
 
 # ------------------------------------------------------------------ paged views
@@ -57,7 +59,7 @@ def store(k_u16: np.ndarray, m32: np.ndarray, fmt: str = "fp32") -> Tuple[np.nda
     return quantise_rows(y, fmt)
 
 
-SCALE_FORMATS = ("fp32", "e8m0", "none")
+SCALE_FORMATS = ("fp32", "e8m0", "none", "bf16")
 
 
 def e8m0_decode(b: np.ndarray) -> np.ndarray:
@@ -69,9 +71,13 @@ def quantise_rows(y: np.ndarray, fmt: str = "fp32") -> Tuple[np.ndarray, np.ndar
     """Per-row (last axis) absmax scaling to the E4M3FN range.
 
     Returns (codes uint8 [..., S], stored scales): float32 for "fp32", uint8
-    E8M0 bytes for "e8m0", None for "none"."""
+    E8M0 bytes for "e8m0", None for "none".  "bf16" returns the bf16 values of
+    y as bytes (uint8 [..., 2S], little-endian) and no scale."""
     if fmt == "none":
         return fp8.encode(y), None
+    if fmt == "bf16":
+        h = f64_to_bf16(y)
+        return np.ascontiguousarray(h).view(np.uint8).reshape(h.shape[:-1] + (2 * h.shape[-1],)), None
     a = np.max(np.abs(y), axis=-1)
     scale = (a / fp8.MAX_FINITE).astype(np.float32)
     s64 = scale.astype(np.float64)
@@ -92,7 +98,7 @@ def quantise_rows(y: np.ndarray, fmt: str = "fp32") -> Tuple[np.ndarray, np.ndar
 
 def scale_multiplier(stored, fmt: str = "fp32"):
     """Stored scales -> the factor the score is multiplied by (fp64)."""
-    if fmt == "none":
+    if fmt in ("none", "bf16"):
         return 1.0
     if fmt == "e8m0":
         return e8m0_decode(stored)
@@ -108,9 +114,19 @@ def project_query(q_u16: np.ndarray, m32: np.ndarray, group: int) -> np.ndarray:
     return np.einsum("hrd,hd->hr", m, qbar)
 
 
+def decode_keys(codes: np.ndarray, fmt: str = "fp32") -> np.ndarray:
+    """Stored projected-key elements -> fp64 values before the scale: FP8 codes
+    [..., S], or for "bf16" the bytes [..., 2S] of S bf16 values."""
+    if fmt == "bf16":
+        c = np.ascontiguousarray(codes)
+        return bf16_to_f64(c.view(np.uint16).reshape(c.shape[:-1] + (c.shape[-1] // 2,)))
+    return fp8.decode(codes)
+
+
 def scores(qhat: np.ndarray, codes: np.ndarray, scale, fmt: str = "fp32") -> np.ndarray:
-    """Projected scores of one KV head: qhat [r], codes [N, r], stored scales [N] -> [N] fp64."""
-    s = scale_multiplier(scale, fmt) * (fp8.decode(codes) @ qhat)
+    """Projected scores of one KV head: qhat [r], codes [N, r] (bf16: [N, 2r] bytes), stored scales [N]
+    -> [N] fp64."""
+    s = scale_multiplier(scale, fmt) * (decode_keys(codes, fmt) @ qhat)
     return np.where(s == 0.0, 0.0, s)
 
 

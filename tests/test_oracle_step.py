@@ -360,7 +360,48 @@ def test_unscaled_format_stores_the_projection_itself():
     assert np.allclose(gqa.scores(q, codes, None, "none"), fp8.decode(codes) @ q, rtol=0, atol=0)
 
 
-@pytest.mark.parametrize("fmt", ["e8m0", "none"])
+def _normal_bf16_patterns():
+    u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    e = (u >> 7) & 0xFF
+    return u[(e >= 1) & (e <= 254)]
+
+
+def test_bf16_rounding_round_trips_every_normal_value_and_zero():
+    u = _normal_bf16_patterns()
+    assert np.array_equal(cal.f64_to_bf16(cal.bf16_to_f64(u)), u)
+    assert cal.f64_to_bf16(np.array([0.0]))[0] == 0 and cal.f64_to_bf16(np.array([-0.0]))[0] == 0x8000
+
+
+def test_bf16_rounding_is_nearest_with_ties_to_even():
+    u = _normal_bf16_patterns()
+    u = u[(u & 0x7F) != 0x7F]                           # neighbour u + 1 in the same binade
+    lo, hi = cal.bf16_to_f64(u), cal.bf16_to_f64(u + 1)
+    mid = (lo + hi) / 2                                  # exact in fp64
+    even = np.where((u & 1) == 0, u, u + 1)
+    assert np.array_equal(cal.f64_to_bf16(mid), even)
+    step = (hi - lo) * 2.0 ** -20                        # toward hi (signed: negative values grow downward)
+    assert np.array_equal(cal.f64_to_bf16(mid - step), u)
+    assert np.array_equal(cal.f64_to_bf16(mid + step), u + 1)
+    # a binade's last value and the next power of two
+    assert cal.f64_to_bf16(np.array([1.0 + 255 / 256 * 1.0]))[0] == 0x4000      # 1.99609375 -> 2.0 (tie to even)
+    with pytest.raises(ValueError):
+        cal.f64_to_bf16(np.array([1e39]))
+
+
+def test_bf16_format_stores_the_rounded_projection_and_scores_it():
+    rng = np.random.default_rng(7)
+    y = rng.standard_normal((50, 32)) * np.exp(rng.uniform(-10, 10, (50, 1)))
+    codes, stored = gqa.quantise_rows(y, "bf16")
+    assert stored is None and codes.dtype == np.uint8 and codes.shape == (50, 64)
+    h = cal.f64_to_bf16(y)
+    assert np.array_equal(codes[:, 0::2], (h & 0xFF).astype(np.uint8))          # little-endian bytes
+    assert np.array_equal(codes[:, 1::2], (h >> 8).astype(np.uint8))
+    assert np.all(np.abs(gqa.decode_keys(codes, "bf16") - y) <= np.abs(y) * 2.0 ** -8)   # half an ulp of 8 bits
+    q = rng.standard_normal(32)
+    assert np.array_equal(gqa.scores(q, codes, None, "bf16"), cal.bf16_to_f64(h) @ q)
+
+
+@pytest.mark.parametrize("fmt", ["e8m0", "none", "bf16"])
 def test_scale_formats_keep_the_needles(fmt):
     """Every planted needle is still selected with the coarser scoring caches."""
     from synth import WORKLOADS, make_gqa_case, make_gqa_calibration, bf16_bits
