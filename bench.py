@@ -63,7 +63,8 @@ def _src_hash(*names):
 
 # ----------------------------------------------------------------------------- algorithmic bytes
 
-SCALE_BYTES = {"fp32": 4, "e8m0": 1, "none": 0}
+SCALE_BYTES = {"fp32": 4, "e8m0": 1, "none": 0, "bf16": 0}
+KEY_BYTES = {"fp32": 1, "e8m0": 1, "none": 1, "bf16": 2}        # bytes per scoring dim
 
 
 def layer_bytes(w, seq_lens, mode, scale_format="fp32"):
@@ -77,6 +78,7 @@ def layer_bytes(w, seq_lens, mode, scale_format="fp32"):
         io_w = w.batch * hq * (d + w.v_dim) * 2 + w.batch * (-(-w.window // w.page_size)) * 4
         return {"kv": sum(min(n, w.window) * hkv * row for n in seq_lens), "q_out_table": io_w}
     sb = SCALE_BYTES[scale_format]
+    S = S * KEY_BYTES[scale_format]
     return {"score": sum(n * hkv * (S + sb) for n in seq_lens),
             "selected_kv": sum(min(B, n) * hkv * row for n in seq_lens),
             "indices": w.batch * hkv * B * 4 * 2,
@@ -495,8 +497,9 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=-1,
                     help="sequences per CPU-oracle pass (0: skip; default the whole batch on the default workload)")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing")
-    ap.add_argument("--scale-format", default="fp32", choices=["fp32", "e8m0", "none"],
-                    help="scoring-cache scale: fp32 per token (default), one-byte power of two, or none")
+    ap.add_argument("--scale-format", default="fp32", choices=["fp32", "e8m0", "none", "bf16"],
+                    help="scoring-cache format: FP8 with an fp32 scale per token (default), with a one-byte power of two, "
+                         "with no scale, or BF16 projected keys")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reference for counter scaling)")
     ap.add_argument("--recall-sweep", action="store_true",
@@ -657,7 +660,7 @@ def main():
            "head_dim": w.head_dim, "seq_len": w.seq_len, "page_size": w.page_size, "rank": w.rank,
            "budget": w.budget, "kv_dtype": "bf16",
            "scoring_cache": {"fp32": "fp8 e4m3fn + fp32 scale per token", "e8m0": "fp8 e4m3fn + e8m0 scale byte",
-                             "none": "fp8 e4m3fn, no scale"}[args.scale_format],
+                             "none": "fp8 e4m3fn, no scale", "bf16": "bf16 projected keys, no scale"}[args.scale_format],
            "replicas": n_rep}
     if w.window:
         cfg.update(layers=w.num_layers, window=w.window, window_layers=list(w.window_layers()))

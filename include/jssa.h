@@ -49,6 +49,11 @@
  *   kp[p][h][i/16][s][i%16] * scale(kp_scale[p][h][s]).  The one-byte and
  *   scale-free forms move the footprint toward the README page's r bytes per
  *   token and KV head ("Notes").
+ *   JSSA_KEYS_BF16 (the README page's jssa_fp8_projk off: BF16 projected keys)
+ *   stores y itself rounded to bf16, two bytes per element and no scale array
+ *   (NULL): kp uint8 [num_pages, Hkv, 2S/16, page, 16], element i in the
+ *   little-endian bytes 2i, 2i + 1 of the token's 2S bytes (the layout above
+ *   with 2S one-byte elements).
  */
 #ifndef JSSA_H_
 #define JSSA_H_
@@ -81,8 +86,9 @@ enum { JSSA_KIND_GQA = 0, JSSA_KIND_MLA = 1 };
  *                 (several passes over the FP8 cache; slow, data independent). */
 enum { JSSA_SELECT_AUTO = 0, JSSA_SELECT_EXACT_STREAM = 1 };
 
-/* jssa_shape.scale_format: the scoring cache's per-(token, KV head) scale. */
-enum { JSSA_SCALE_FP32 = 0, JSSA_SCALE_E8M0 = 1, JSSA_SCALE_NONE = 2 };
+/* jssa_shape.scale_format: the scoring cache's format, FP8 codes with a
+ * per-(token, KV head) scale of one of three kinds, or BF16 keys. */
+enum { JSSA_SCALE_FP32 = 0, JSSA_SCALE_E8M0 = 1, JSSA_SCALE_NONE = 2, JSSA_KEYS_BF16 = 3 };
 
 typedef struct jssa_shape {
   int32_t kind;               /* JSSA_KIND_GQA or JSSA_KIND_MLA */
@@ -95,7 +101,7 @@ typedef struct jssa_shape {
   int32_t rank;               /* r: GQA r % 16 == 0, r <= min(d, 128); MLA latent rank, 64 */
   int32_t budget;             /* B: 1..4096 */
   int32_t select_mode;        /* JSSA_SELECT_AUTO or JSSA_SELECT_EXACT_STREAM */
-  int32_t scale_format;       /* JSSA_SCALE_FP32 (0), JSSA_SCALE_E8M0 or JSSA_SCALE_NONE */
+  int32_t scale_format;       /* JSSA_SCALE_FP32 (0), JSSA_SCALE_E8M0, JSSA_SCALE_NONE or JSSA_KEYS_BF16 */
 } jssa_shape;
 
 /* Human-readable name of a jssa_status value (static string, never NULL). */
@@ -108,7 +114,7 @@ int32_t jssa_workspace_bytes(const jssa_shape* shape, size_t* bytes);
 
 /* Bytes of the projected scoring cache per page (kp) and scale elements per
  * page (kp_scale: fp32 for JSSA_SCALE_FP32, bytes for JSSA_SCALE_E8M0, 0 for
- * JSSA_SCALE_NONE), so callers can size both buffers. */
+ * JSSA_SCALE_NONE and JSSA_KEYS_BF16), so callers can size both buffers. */
 int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page,
                            int64_t* scale_elems_per_page);
 
@@ -119,12 +125,13 @@ int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page,
  *   nearest even, saturating; an all-zero y stores scale 0 and zero codes.
  *   JSSA_SCALE_E8M0: the scale is rounded up to a power of two 2^e (e = ceil
  *   log2 of the fp32 scale, clamped to [-127, 127]; stored byte e + 127, 0 for
- *   a zero row) and codes = E4M3FN(y / 2^e); JSSA_SCALE_NONE: codes = E4M3FN(y).
+ *   a zero row) and codes = E4M3FN(y / 2^e); JSSA_SCALE_NONE: codes = E4M3FN(y);
+ *   JSSA_KEYS_BF16: y rounded to bf16 (nearest, ties to even), no scale.
  * k_new : GQA bf16 [T, Hkv, d]; MLA bf16 [T, 576]
  * slot  : int32 [T], physical page * page_size + slot in page; < 0 skips the row
  * M     : GQA fp32 [Hkv, r, d]; MLA fp32 [r, 512]
  * kp, kp_scale : the scoring cache (layout above), written at the slots only
- *                (kp_scale may be NULL with JSSA_SCALE_NONE). */
+ *                (kp_scale may be NULL with JSSA_SCALE_NONE or JSSA_KEYS_BF16). */
 int32_t jssa_store(const jssa_shape* shape, const uint16_t* k_new, const int32_t* slot, int32_t T,
                    const float* M, uint8_t* kp, void* kp_scale, hipStream_t stream);
 

@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(_PKG, "libjssa.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 KIND_GQA, KIND_MLA = 0, 1
 SELECT_AUTO, SELECT_EXACT_STREAM = 0, 1
-SCALE_FP32, SCALE_E8M0, SCALE_NONE = 0, 1, 2
-SCALE_FORMATS = {"fp32": SCALE_FP32, "e8m0": SCALE_E8M0, "none": SCALE_NONE}
+SCALE_FP32, SCALE_E8M0, SCALE_NONE, KEYS_BF16 = 0, 1, 2, 3
+SCALE_FORMATS = {"fp32": SCALE_FP32, "e8m0": SCALE_E8M0, "none": SCALE_NONE, "bf16": KEYS_BF16}
 STAGE_PROLOGUE, STAGE_STREAM, STAGE_FINISH, STAGE_ALL = 1, 2, 4, 7
 MLA_LATENT, MLA_ROPE = 512, 64
 
@@ -133,11 +133,17 @@ def _scale_dtype(shape: Shape):
     return {SCALE_FP32: torch.float32, SCALE_E8M0: torch.uint8}.get(shape.scale_format)
 
 
+def _kp_pieces(shape: Shape) -> int:
+    """16-byte pieces per (token, KV head): S/16 FP8 codes, 2S/16 for BF16 keys."""
+    return shape.score_dims // 16 * (2 if shape.scale_format == KEYS_BF16 else 1)
+
+
 def alloc_scoring_cache(shape: Shape, num_pages: int, device="cuda") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Zeroed projected scoring cache: kp uint8 [num_pages, Hkv, S/16, page, 16] and the scales
-    [num_pages, Hkv, page] (fp32, or uint8 E8M0 bytes; None when the format has no scale)."""
-    s = shape.score_dims
-    kp = torch.zeros((num_pages, shape.num_kv_heads, s // 16, shape.page_size, 16), dtype=torch.uint8, device=device)
+    """Zeroed projected scoring cache: kp uint8 [num_pages, Hkv, S/16, page, 16] (BF16 keys: 2S/16
+    pieces) and the scales [num_pages, Hkv, page] (fp32, or uint8 E8M0 bytes; None when the format has
+    no scale)."""
+    kp = torch.zeros((num_pages, shape.num_kv_heads, _kp_pieces(shape), shape.page_size, 16), dtype=torch.uint8,
+                     device=device)
     dt = _scale_dtype(shape)
     sc = None if dt is None else torch.zeros((num_pages, shape.num_kv_heads, shape.page_size), dtype=dt, device=device)
     return kp, sc
@@ -181,7 +187,6 @@ def _m_shape(shape: Shape):
 
 def _kp_args(shape: Shape, kp: torch.Tensor, kp_scale: Optional[torch.Tensor]):
     n = kp.shape[0]
-    s = shape.score_dims
     dt = _scale_dtype(shape)
     if dt is None:
         if kp_scale is not None:
@@ -189,7 +194,7 @@ def _kp_args(shape: Shape, kp: torch.Tensor, kp_scale: Optional[torch.Tensor]):
         sc = ctypes.c_void_p(0)
     else:
         sc = _ptr("kp_scale", kp_scale, dt, (n, shape.num_kv_heads, shape.page_size))
-    return (_ptr("kp", kp, torch.uint8, (n, shape.num_kv_heads, s // 16, shape.page_size, 16)), sc)
+    return (_ptr("kp", kp, torch.uint8, (n, shape.num_kv_heads, _kp_pieces(shape), shape.page_size, 16)), sc)
 
 
 def _ws(shape: Shape, workspace: torch.Tensor):

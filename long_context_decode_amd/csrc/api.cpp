@@ -61,6 +61,9 @@ void mla_dense_plan(int64_t n, int batch, int Hq, int* splits, int* len) {
   *splits = (int)cdiv(n, *len);
 }
 
+// formats without a scale array
+bool scale_free(int sfmt) { return sfmt == JSSA_SCALE_NONE || sfmt == JSSA_KEYS_BF16; }
+
 int32_t validate_shape(const jssa_shape* sh) {
   if (!sh) return JSSA_ERR_NULL;
   if (sh->kind != JSSA_KIND_GQA && sh->kind != JSSA_KIND_MLA) return JSSA_ERR_UNSUPPORTED;
@@ -71,7 +74,7 @@ int32_t validate_shape(const jssa_shape* sh) {
   if (sh->page_size != 16 && sh->page_size != 32 && sh->page_size != 64) return JSSA_ERR_UNSUPPORTED;
   if (sh->select_mode != JSSA_SELECT_AUTO && sh->select_mode != JSSA_SELECT_EXACT_STREAM) return JSSA_ERR_SHAPE;
   if (sh->scale_format != JSSA_SCALE_FP32 && sh->scale_format != JSSA_SCALE_E8M0 &&
-      sh->scale_format != JSSA_SCALE_NONE)
+      sh->scale_format != JSSA_SCALE_NONE && sh->scale_format != JSSA_KEYS_BF16)
     return JSSA_ERR_UNSUPPORTED;
   if (sh->rank < 16 || sh->rank % 16 != 0) return JSSA_ERR_UNSUPPORTED;
   if (sh->kind == JSSA_KIND_GQA) {
@@ -106,7 +109,9 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   p->dv = p->mla ? kMlaLatent : p->d;
   p->maxN = (int64_t)p->max_pages * p->P;
   // stream chunking: one wavefront per chunk of 4 groups of 16 / (S / 16) pages
-  p->cp = 4 * std::max(1, 16 / (p->S / 16));
+  // stream chunk: 4 wavefronts x 16 / (16-byte pieces per token) pages
+  const int pieces = (p->sfmt == JSSA_KEYS_BF16 ? 2 : 1) * (p->S / 16);
+  p->cp = 4 * std::max(1, 16 / pieces);
   p->max_chunks = (int)cdiv(p->max_pages, p->cp);
   if (p->max_chunks > kMaxChunks) return JSSA_ERR_UNSUPPORTED;
   split_plan(std::min<int64_t>(p->B, p->maxN), p->batch * p->Hkv, &p->sp_splits, &p->sp_len);
@@ -158,7 +163,7 @@ int32_t do_store(const Plan& p, const uint16_t* k_new, const int32_t* slot, int3
                  uint8_t* kp, void* kp_scale, hipStream_t stream) {
   if (T < 0) return JSSA_ERR_SHAPE;
   if (T == 0) return JSSA_OK;
-  if (!k_new || !slot || !M || !kp || (!kp_scale && p.sfmt != JSSA_SCALE_NONE)) return JSSA_ERR_NULL;
+  if (!k_new || !slot || !M || !kp || (!kp_scale && !scale_free(p.sfmt))) return JSSA_ERR_NULL;
   StoreArgs a{};
   a.k_new = k_new;
   a.slot = slot;
@@ -180,7 +185,7 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
                   const void* kp_scale, const int32_t* block_table, const int32_t* seq_lens, int32_t* indices,
                   float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream, const uint16_t* k_new = nullptr,
                   const int32_t* slot_new = nullptr) {
-  if (!q || !M || !kp || (!kp_scale && p.sfmt != JSSA_SCALE_NONE) || !block_table || !seq_lens || !indices || !ws)
+  if (!q || !M || !kp || (!kp_scale && !scale_free(p.sfmt)) || !block_table || !seq_lens || !indices || !ws)
     return JSSA_ERR_NULL;
   if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
   SelectArgs a{};
@@ -300,8 +305,8 @@ int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page, 
   Plan p;
   const int32_t st = make_plan(shape, &p);
   if (st != JSSA_OK) return st;
-  *kp_bytes_per_page = (int64_t)p.Hkv * p.P * p.S;
-  *scale_elems_per_page = p.sfmt == JSSA_SCALE_NONE ? 0 : (int64_t)p.Hkv * p.P;
+  *kp_bytes_per_page = (int64_t)p.Hkv * p.P * p.S * (p.sfmt == JSSA_KEYS_BF16 ? 2 : 1);
+  *scale_elems_per_page = scale_free(p.sfmt) ? 0 : (int64_t)p.Hkv * p.P;
   return JSSA_OK;
 }
 
@@ -354,7 +359,7 @@ int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
   int32_t st = make_plan(shape, &p);
   if (st != JSSA_OK) return st;
   // validate everything before the first launch
-  if (!q || !M || !kp || (!kp_scale && p.sfmt != JSSA_SCALE_NONE) || !k_cache || !block_table || !seq_lens ||
+  if (!q || !M || !kp || (!kp_scale && !scale_free(p.sfmt)) || !k_cache || !block_table || !seq_lens ||
       !indices || !out || !workspace)
     return JSSA_ERR_NULL;
   if (!p.mla && !v_cache) return JSSA_ERR_NULL;

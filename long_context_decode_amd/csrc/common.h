@@ -82,7 +82,7 @@ __device__ __forceinline__ float proj_combine(float v) {
 }
 
 // Scale of one projected key (scoring-cache format sfmt: 0 fp32, 1 E8M0, 2
-// none).  Returns the divisor of y (0 for an all-zero row of a scaled format)
+// none; 3, BF16 keys, has no scale and does not quantise).  Returns the divisor of y (0 for an all-zero row of a scaled format)
 // and the stored representation: fp32 bits, the E8M0 byte e + 127 with
 // e = ceil(log2(amax / 448)) clamped to [-127, 127], or nothing.
 __device__ __forceinline__ float quant_divisor(float amax, int sfmt, uint32_t* stored) {
@@ -112,7 +112,8 @@ __device__ __forceinline__ void store_scale(void* base, int64_t i, int sfmt, uin
   else if (sfmt == 1) static_cast<uint8_t*>(base)[i] = (uint8_t)stored;
 }
 
-// The factor a score is multiplied by: the fp32 scale, 2^(E - 127), or 1.
+// The factor a score is multiplied by: the fp32 scale, 2^(E - 127), or 1 (no
+// scale, BF16 keys).
 // (E8M0 scale arrays start 4-byte aligned; the word of element i lies inside
 // the array because the page size is a multiple of 4.)
 __device__ __forceinline__ float load_scale(const void* base, int64_t i, int sfmt) {
@@ -126,7 +127,8 @@ __device__ __forceinline__ float load_scale(const void* base, int64_t i, int sfm
 }
 
 // Byte offset of element o of the projected key at (page, head, slot) in the
-// piece-major scoring cache [pages][Hkv][S/16][P][16].
+// piece-major scoring cache [pages][Hkv][S/16][P][16] (BF16 keys: the bytes
+// 2o, 2o + 1 of a cache of 2S bytes per token).
 __device__ __forceinline__ int64_t kp_offset(int64_t page, int head, int slot, int o, int Hkv, int S, int P) {
   return (page * Hkv + head) * ((int64_t)S * P) + (o >> 4) * (P * 16) + slot * 16 + (o & 15);
 }
@@ -153,6 +155,36 @@ __device__ __forceinline__ float score_pieces(const uint4 (&pc)[R], const float*
     }
   }
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// The same score over BF16 projected keys (the scoring-cache format without
+// FP8, two bytes per element): RP = 2 x scoring dims / 16 pieces of 8 values;
+// chain e takes the elements i with i % 8 in {2e, 2e + 1}.
+template <int RP>
+__device__ __forceinline__ float score_pieces_bf16(const uint4 (&pc)[RP], const float* qh) {
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < RP; ++j) {
+    const uint32_t w[4] = {pc[j].x, pc[j].y, pc[j].z, pc[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = __builtin_fmaf(bf16_lo(w[e]), qh[j * 8 + e * 2], acc[e]);
+      acc[e] = __builtin_fmaf(bf16_hi(w[e]), qh[j * 8 + e * 2 + 1], acc[e]);
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// 16-byte pieces per token and KV head: S/16 FP8 codes, or 2S/16 for BF16 keys.
+template <int R, bool BF>
+struct TokenPieces {
+  static constexpr int value = BF ? 2 * R : R;
+};
+
+template <int R, bool BF>
+__device__ __forceinline__ float score_token(const uint4 (&pc)[TokenPieces<R, BF>::value], const float* qh) {
+  if constexpr (BF) return score_pieces_bf16<2 * R>(pc, qh);
+  else return score_pieces<R>(pc, qh);
 }
 
 // Order-preserving float -> uint32 map; -0 and +0 share one key.  Finite

@@ -154,6 +154,7 @@ __device__ void block_radix_select(const uint32_t* keys, int n, uint32_t k, uint
 
 // ------------------------------------------------------------------ token access
 
+// the token's R 16-byte pieces (R = TokenPieces) and its scale (1 without one)
 template <int R>
 __device__ __forceinline__ void load_token(const SelectArgs& a, int64_t phys, int head, int slot, uint4 (&pc)[R],
                                            float& sc) {
@@ -173,13 +174,14 @@ __device__ __forceinline__ void load_token_sf(const SelectArgs& a, int64_t phys,
   sc = load_scale(a.kp_scale, (phys * a.Hkv + head) * a.P + slot, SF);
 }
 
-template <int R>
+template <int R, bool BF>
 __device__ __forceinline__ uint32_t token_key(const SelectArgs& a, int b, int head, int t, const float* qh) {
+  constexpr int RP = TokenPieces<R, BF>::value;
   const int64_t phys = a.block_table[(int64_t)b * a.max_pages + t / a.P];
-  uint4 pc[R];
+  uint4 pc[RP];
   float sc;
-  load_token<R>(a, phys, head, t % a.P, pc, sc);
-  return score_key(score_pieces<R>(pc, qh) * sc);
+  load_token<RP>(a, phys, head, t % a.P, pc, sc);
+  return score_key(score_token<R, BF>(pc, qh) * sc);
 }
 
 __device__ __forceinline__ int seq_len_of(const SelectArgs& a, int b) {
@@ -192,10 +194,11 @@ __device__ __forceinline__ int seq_len_of(const SelectArgs& a, int b) {
 
 // ================================================================== 1. prologue
 
-template <int R>
+template <int R, bool BF>
 __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a) {
   constexpr int S = R * 16;
-  constexpr int TPT = R >= 8 ? 1 : 8 / R;      // sampled tokens per thread with loads in flight together
+  constexpr int RP = TokenPieces<R, BF>::value;
+  constexpr int TPT = RP >= 8 ? 1 : 8 / RP;    // sampled tokens per thread with loads in flight together
   const int h = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
   __shared__ double qbar[kMlaLatent + kMlaRope];
   __shared__ double qpart[8 * (kMlaLatent + kMlaRope)];   // head-group partials of qbar (G <= 128)
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   // entries of every round first (with the query loads), then each round's
   // FP8 rows (round 0 as soon as the query is summed).  Round r covers the
   // sample indices u = (r TPT + j) threads + tid, j < TPT.
-  uint4 pc[TPT][R];
+  uint4 pc[TPT][RP];
   float sc[TPT];
   constexpr int KS = kSampleMax / kPrologueThreads;
   int ph[KS];
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
       const int u = (r * TPT + j) * kPrologueThreads + tid;
-      if (u < ns && sph[u] >= 0) load_token<R>(a, sph[u], h, u % a.P, pc[j], sc[j]);
+      if (u < ns && sph[u] >= 0) load_token<RP>(a, sph[u], h, u % a.P, pc[j], sc[j]);
     }
   };
 
@@ -376,7 +379,12 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
       a.qhat[bh * S + o] = (float)v;
     }
   }
-  if (new_slot >= 0 && tid < 64) {
+  if (BF && new_slot >= 0 && tid < S) {        // BF16 keys: y rounded, no scale
+    const int page = new_slot / a.P, sip = new_slot % a.P;
+    *reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(a.kp) + kp_offset(page, h, sip, 2 * tid, a.Hkv, 2 * S, a.P)) =
+        f32_to_bf16(ynew[tid]);
+  }
+  if (!BF && new_slot >= 0 && tid < 64) {
     float am = 0.0f;
     for (int o = tid; o < S; o += 64) am = fmaxf(am, fabsf(ynew[o]));
     am = wave_max(am);
@@ -403,7 +411,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 #pragma unroll
       for (int j = 0; j < TPT; ++j) {
         const int u = (r * TPT + j) * kPrologueThreads + tid;
-        if (u < ns) skeys[u] = sph[u] >= 0 ? score_key(score_pieces<R>(pc[j], qh) * sc[j]) : 0u;
+        if (u < ns) skeys[u] = sph[u] >= 0 ? score_key(score_token<R, BF>(pc[j], qh) * sc[j]) : 0u;
       }
     }
     // sampled pages are full pages except when every page is sampled (then
@@ -428,8 +436,10 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 template <int R, int P, int SF>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(R <= 2 ? 4 : 1))) void select_stream(SelectArgs a) {
   constexpr int S = R * 16;
+  constexpr bool BF = SF == 3;              // BF16 keys
+  constexpr int RP = TokenPieces<R, BF>::value;
   constexpr int HPW = 64 / P;               // KV heads covered by one wavefront
-  constexpr int PF = R >= 16 ? 1 : 16 / R;  // pages of a wavefront (all in flight at once)
+  constexpr int PF = RP >= 16 ? 1 : 16 / RP;  // pages of a wavefront (all in flight at once)
   __shared__ uint32_t wcnt[4][HPW];
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
   const int hg = blockIdx.x, c = blockIdx.y, b = blockIdx.z;   // chunk c = 4 wavefronts
@@ -447,12 +457,12 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
   // physical pages of this wavefront: lane i < PF holds page page0 + i
   int phys_l = 0;
   if (lane < PF && page0 + lane < n_pages) phys_l = a.block_table[(int64_t)b * a.max_pages + page0 + lane];
-  uint4 pc[PF][R];
+  uint4 pc[PF][RP];
   float sc[PF];
 #pragma unroll
   for (int f = 0; f < PF; ++f) {
     const int64_t phys = __builtin_amdgcn_readlane(phys_l, f);
-    if (active && page0 + f < n_pages) load_token_sf<R, SF>(a, phys, head, slot, pc[f], sc[f]);
+    if (active && page0 + f < n_pages) load_token_sf<RP, SF>(a, phys, head, slot, pc[f], sc[f]);
   }
   float qh[S];
   {
@@ -481,7 +491,7 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
     const int t = (page0 + f) * P + slot;
     key[f] = 0u;
     if (any && active && t < N) {
-      const float s = score_pieces<R>(pc[f], qh) * sc[f];
+      const float s = score_token<R, BF>(pc[f], qh) * sc[f];
       key[f] = score_key(s);
       if (sout) sout[t] = s;
     }
@@ -514,7 +524,7 @@ namespace {
 
 // Exact top-K of one (sequence, KV head) by re-scoring every token: four
 // 8-bit radix passes over the keys, then an ordered compaction pass.
-template <int R>
+template <int R, bool BF>
 __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, int K, const float* qh,
                                     uint32_t* hist, uint32_t* tmp, int32_t* out) {
   const int tid = (int)threadIdx.x;
@@ -526,7 +536,7 @@ __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, in
       asm volatile("" ::: "memory");   // qh is re-read from LDS, not held in registers
       const int t = t0 + tid;
       if (t < N) {
-        const uint32_t key = token_key<R>(a, b, h, t, qh);
+        const uint32_t key = token_key<R, BF>(a, b, h, t, qh);
         if ((key & hi_mask) == prefix) atomicAdd(&hist[bin_slot((key >> shift) & (kBins - 1u))], 1u);
       }
     }
@@ -545,7 +555,7 @@ __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, in
   for (int t0 = 0; t0 < N; t0 += kFinishThreads) {
     asm volatile("" ::: "memory");
     const int t = t0 + tid;
-    const uint32_t key = t < N ? token_key<R>(a, b, h, t, qh) : 0u;
+    const uint32_t key = t < N ? token_key<R, BF>(a, b, h, t, qh) : 0u;
     const uint32_t gt = key > kth ? 1u : 0u, eq = (t < N && key == kth) ? 1u : 0u;
     uint32_t tot;
     const uint32_t ex = block_excl_scan<kFinishThreads>(gt | (eq << 16), tmp, &tot);
@@ -559,7 +569,7 @@ __device__ void exact_stream_select(const SelectArgs& a, int b, int h, int N, in
 
 }  // namespace
 
-template <int R>
+template <int R, bool BF>
 __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   constexpr int S = R * 16;
   const int h = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x;
@@ -607,7 +617,7 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   if (!ok) {
     for (int i = tid; i < S; i += kFinishThreads) qh[i] = a.qhat[bh * S + i];
     __syncthreads();
-    exact_stream_select<R>(a, b, h, N, K, qh, hist, tmp, out);
+    exact_stream_select<R, BF>(a, b, h, N, K, qh, hist, tmp, out);
     return;
   }
   if (tid == 0) coff[n_chunks] = carry;
@@ -682,18 +692,20 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
 
 namespace {
 
-template <int R, int P>
-hipError_t launch_select_rp(const SelectArgs& a, int stages, hipStream_t s) {
+template <int R, int P, bool BF>
+hipError_t launch_select_rpb(const SelectArgs& a, int stages, hipStream_t s) {
   constexpr int HPW = 64 / P;
   hipError_t e = hipSuccess;
   if (stages & 1) {
-    hipLaunchKernelGGL(select_prologue<R>, dim3(a.Hkv, a.batch), dim3(kPrologueThreads), 0, s, a);
+    hipLaunchKernelGGL((select_prologue<R, BF>), dim3(a.Hkv, a.batch), dim3(kPrologueThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2) {
     const int hg = (a.Hkv + HPW - 1) / HPW;
     const dim3 grid(hg, a.max_chunks, a.batch);
-    if (a.sfmt == 1)
+    if (BF)
+      hipLaunchKernelGGL((select_stream<R, P, 3>), grid, dim3(kStreamThreads), 0, s, a);
+    else if (a.sfmt == 1)
       hipLaunchKernelGGL((select_stream<R, P, 1>), grid, dim3(kStreamThreads), 0, s, a);
     else if (a.sfmt == 2)
       hipLaunchKernelGGL((select_stream<R, P, 2>), grid, dim3(kStreamThreads), 0, s, a);
@@ -702,10 +714,15 @@ hipError_t launch_select_rp(const SelectArgs& a, int stages, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4) {
-    hipLaunchKernelGGL(select_finish<R>, dim3(a.Hkv, a.batch), dim3(kFinishThreads), 0, s, a);
+    hipLaunchKernelGGL((select_finish<R, BF>), dim3(a.Hkv, a.batch), dim3(kFinishThreads), 0, s, a);
     e = hipGetLastError();
   }
   return e;
+}
+
+template <int R, int P>
+hipError_t launch_select_rp(const SelectArgs& a, int stages, hipStream_t s) {
+  return a.sfmt == 3 ? launch_select_rpb<R, P, true>(a, stages, s) : launch_select_rpb<R, P, false>(a, stages, s);
 }
 
 template <int R>

@@ -3,7 +3,9 @@
 // scoring cache (paper summary page, §3.4 Projected Scoring Cache:
 // K_proj = K M^T kept in FP8; MLA scores on 64 latent + 64 RoPE dims).
 //
-// The scale format (fp32, one-byte power of two, none) follows the shape.
+// The scale format (fp32, one-byte power of two, none) follows the shape; the
+// BF16-key format stores y itself rounded to bf16 (two bytes per element, no
+// scale).
 //
 // One wavefront per (new token, KV head).  The projected outputs are done
 // eight at a time: lane l takes part l & 7 of output 8 pass + (l >> 3)
@@ -47,6 +49,18 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
   if (a.mla) {                                        // RoPE dims: lane l -> output r + l
     yr = bf16_to_f32(row[kMlaLatent + lane]);
     amax = fmaxf(amax, fabsf(yr));
+  }
+  if (a.sfmt == 3) {                                  // BF16 keys: y rounded, no scale
+#pragma unroll
+    for (int p = 0; p < kMaxPasses; ++p) {
+      if (p < passes && part == 0)
+        *reinterpret_cast<uint16_t*>(a.kp + kp_offset(page, h, sip, 2 * (p * 8 + oi), a.Hkv, 2 * a.S, a.P)) =
+            f32_to_bf16(y[p]);
+    }
+    if (a.mla)
+      *reinterpret_cast<uint16_t*>(a.kp + kp_offset(page, h, sip, 2 * (a.r + lane), a.Hkv, 2 * a.S, a.P)) =
+          f32_to_bf16(yr);
+    return;
   }
   amax = wave_max(amax);
   uint32_t stored;

@@ -65,6 +65,11 @@ def test_workspace_and_page_sizes():
     assert L.kp_page_bytes(s) == (8 * 16 * 32, 8 * 16)
     m = _shape(kind=1, num_kv_heads=1, num_q_heads=128, head_dim=576, rank=64, page_size=64)
     assert L.kp_page_bytes(m) == (64 * 128, 64)
+    # scale-free formats: no scale elements; BF16 keys take two bytes per element
+    assert L.kp_page_bytes(_shape(scale_format=L.SCALE_NONE)) == (8 * 16 * 32, 0)
+    assert L.kp_page_bytes(_shape(scale_format=L.KEYS_BF16)) == (2 * 8 * 16 * 32, 0)
+    n = ctypes.c_size_t()
+    assert L.raw_library().jssa_workspace_bytes(ctypes.byref(_shape(scale_format=4)), ctypes.byref(n)) == -3
 
 
 def test_entry_points_reject_before_launch():

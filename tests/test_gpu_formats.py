@@ -1,4 +1,4 @@
-"""GPU parity of the scoring-cache scale formats (one-byte E8M0 scale, no scale).
+"""GPU parity of the scoring-cache formats (one-byte E8M0 scale, no scale, BF16 keys).
 
 For each format: the bulk store through jssa_store against the oracle's store of
 the same format, the selection through jssa_select (both modes) against the
@@ -27,7 +27,7 @@ from util import check_attention, check_codes, check_selection
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-FORMATS = ["e8m0", "none"]
+FORMATS = ["e8m0", "none", "bf16"]
 
 
 def _w(base, **kw):
@@ -83,6 +83,23 @@ def _near_power_of_two(s32):
     return np.abs(m - 0.5) <= 0.5 * 2.0 ** -20
 
 
+def _check_bf16_keys(gc, oc, y, absdot):
+    """BF16 keys: the GPU rounds its fp32 projection, the oracle the exact one.  Every stored value is
+    within the fp32 dot-product error bound (terms x 2^-24 x sum |m_i k_i|) plus half a bf16 step of y;
+    at most 1% of the values differ from the oracle's bf16 at all."""
+    gv = ogqa.decode_keys(gc, "bf16")
+    bound = absdot * 2.0 ** -24 + np.abs(y) * 2.0 ** -8
+    assert np.all(np.abs(gv - y) <= bound), float(np.max(np.abs(gv - y) - bound))
+    assert float(np.mean(gc != oc)) <= 1e-2
+
+
+def _projection(rows_u16, m32):
+    """Exact projection y = M k and the bound's sum (terms) x |M| |k| of one KV head's rows."""
+    k = ocal.bf16_to_f64(rows_u16)
+    m = np.asarray(m32, np.float32).astype(np.float64)
+    return k @ m.T, k.shape[1] * (np.abs(k) @ np.abs(m).T)
+
+
 def _check_store(fmt, gc, gs, oc, os_, s32_ref):
     """Codes within one step of the oracle's; E8M0 bytes equal except near a power of two."""
     keep = np.ones(len(oc), bool)
@@ -118,7 +135,9 @@ def test_format_store_and_select(name, fmt):
             qhat = ogqa.project_query(q[b], m32, w.group)
             for h in range(w.num_kv_heads):
                 gc, gs = _unpack(kp_h, ks_h, bt[b], n, w.page_size, h)
-                if mode == L.SELECT_AUTO:
+                if mode == L.SELECT_AUTO and fmt == "bf16":
+                    _check_bf16_keys(gc, oc[:, h], *_projection(rows_k[b][:, h], m32[h]))
+                elif mode == L.SELECT_AUTO:
                     _check_store(fmt, gc, gs, oc[:, h], None if os_ is None else os_[:, h], o32[:, h])
                 sc = ogqa.scores(qhat[h], gc, gs, fmt)
                 oidx, tau = ogqa.select_topb(sc, w.budget)
@@ -188,7 +207,12 @@ def test_format_mla_store_and_select(fmt):
         oc, os_ = omla.store(rows, m32, fmt=fmt)
         o32 = omla.store(rows, m32)[1]
         gc, gs = _unpack(kp_h, ks_h, bt[b], n, w.page_size, 0)
-        _check_store(fmt, gc, gs, oc, os_, o32)
+        if fmt == "bf16":
+            y, ad = _projection(rows[:, :512], m32)
+            rope = ocal.bf16_to_f64(rows[:, 512:])             # the RoPE dims pass through exactly
+            _check_bf16_keys(gc, oc, np.concatenate([y, rope], 1), np.concatenate([ad, np.zeros_like(rope)], 1))
+        else:
+            _check_store(fmt, gc, gs, oc, os_, o32)
         sc = ogqa.scores(omla.project_query(q[b], m32), gc, gs, fmt)
         oidx, tau = ogqa.select_topb(sc, w.budget)
         check_selection(gidx[b, 0], oidx, sc, tau)
