@@ -423,7 +423,8 @@ def recall_sweep(name, ranks, n_seqs, query_shift=0):
     """Top-B recall of the FP8 projected-score selection against the exact top-B of qbar . k (fp32 scores
     from plain torch on the GPU), for several ranks and three bases per KV head: the joint basis M*
     (jssa_calib_moments + jssa_basis), the top-r eigenvectors of the key moments alone (jssa_basis with the
-    key moments on both sides) and a random orthonormal basis.  Also reports the planted needles found."""
+    key moments on both sides) and a random orthonormal basis; and the joint basis over BF16 projected keys.
+    Also reports the planted needles found."""
     import numpy as np
     import torch
     import long_context_decode_amd as L
@@ -461,12 +462,16 @@ def recall_sweep(name, ranks, n_seqs, query_shift=0):
             "random": np.stack([haar_orthogonal(w.head_dim, 1000 + 7 * h + r)[:, :r].T
                                 for h in range(w.num_kv_heads)]).astype(np.float32),
         }
-        for bname, m in bases.items():
+        # the FP8 cache for every basis, and the joint basis over BF16 keys (the README's non-FP8 option)
+        variants = [(bname, m, L.SCALE_FP32) for bname, m in bases.items()]
+        variants.append(("joint M*, BF16 keys", bases["joint M*"], L.KEYS_BF16))
+        for bname, m, fmt in variants:
+            shp = L.shape_for(w.scaled(rank=r), scale_format=fmt)
             M = torch.from_numpy(np.ascontiguousarray(m)).to(dev)
-            kp, ks = L.alloc_scoring_cache(shape, lay.k_cache.shape[0], dev)
-            bulk_store(L, w, shape, lay.k_cache.view(-1, w.num_kv_heads, w.head_dim), bt, sl, M, kp, ks)
+            kp, ks = L.alloc_scoring_cache(shp, lay.k_cache.shape[0], dev)
+            bulk_store(L, w, shp, lay.k_cache.view(-1, w.num_kv_heads, w.head_dim), bt, sl, M, kp, ks)
             idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=dev)
-            L.jssa_select(shape, lay.q, M, kp, ks, bt, sl, idx, L.alloc_workspace(shape, dev))
+            L.jssa_select(shp, lay.q, M, kp, ks, bt, sl, idx, L.alloc_workspace(shp, dev))
             hits, found, total_n = 0, 0, 0
             for b in range(w.batch):
                 for h in range(w.num_kv_heads):
