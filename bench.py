@@ -449,7 +449,11 @@ def recall_sweep(name, ranks, n_seqs, query_shift=0):
     needles = {k: torch.as_tensor(v, device=dev) for k, v in lay.needles.items()}
     rows = []
     for r in ranks:
-        shape = L.shape_for(w.scaled(rank=r))
+        # ranks below the kernels' 16-dim pieces: the first r rows of the rank-16 basis (rows are in
+        # descending eigenvalue order), zero-padded to 16 rows.  The zero rows add nothing to a score
+        # and leave each token's scale (max |y|) unchanged, so the selection is that of rank r.
+        rk = max(r, 16)
+        shape = L.shape_for(w.scaled(rank=rk))
         T = qc.shape[0]
         gq = torch.zeros((w.num_kv_heads, w.head_dim, w.head_dim), dtype=torch.float32, device=dev)
         gk = torch.zeros_like(gq)
@@ -459,14 +463,16 @@ def recall_sweep(name, ranks, n_seqs, query_shift=0):
         bases = {
             "joint M*": L.jssa_basis(shape, gq_h, gk_h),
             "keys only": L.jssa_basis(shape, gk_h, gk_h),
-            "random": np.stack([haar_orthogonal(w.head_dim, 1000 + 7 * h + r)[:, :r].T
+            "random": np.stack([haar_orthogonal(w.head_dim, 1000 + 7 * h + r)[:, :rk].T
                                 for h in range(w.num_kv_heads)]).astype(np.float32),
         }
+        for m in bases.values():
+            m[:, r:, :] = 0.0
         # the FP8 cache for every basis, and the joint basis over BF16 keys (the README's non-FP8 option)
         variants = [(bname, m, L.SCALE_FP32) for bname, m in bases.items()]
         variants.append(("joint M*, BF16 keys", bases["joint M*"], L.KEYS_BF16))
         for bname, m, fmt in variants:
-            shp = L.shape_for(w.scaled(rank=r), scale_format=fmt)
+            shp = L.shape_for(w.scaled(rank=rk), scale_format=fmt)
             M = torch.from_numpy(np.ascontiguousarray(m)).to(dev)
             kp, ks = L.alloc_scoring_cache(shp, lay.k_cache.shape[0], dev)
             bulk_store(L, w, shp, lay.k_cache.view(-1, w.num_kv_heads, w.head_dim), bt, sl, M, kp, ks)
@@ -509,7 +515,7 @@ def main():
                     help="also run one elementwise kernel over 1 GiB (reference for counter scaling)")
     ap.add_argument("--recall-sweep", action="store_true",
                     help="top-B recall vs rank for the joint, key-only and random bases (prints one JSON line)")
-    ap.add_argument("--ranks", default="16,32,48,64")
+    ap.add_argument("--ranks", default="4,8,16,32,48,64")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--command", default="", help="profiling command recorded in a summary")
