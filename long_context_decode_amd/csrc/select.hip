@@ -11,10 +11,11 @@
 //     candidate buffer).  In jssa_decode it also stores the new token.
 //  2. stream    (each wavefront owns 16/R consecutive pages of one sequence
 //     for a group of KV heads; a block's four wavefronts form one chunk):
-//     every lane owns one (KV head, slot) and reads that token's 16-byte FP8
-//     pieces for all pages at once (a wavefront reads one contiguous run per
-//     piece), scores them, and the keys >= tau are compacted in position
-//     order straight from the ballot masks into the chunk's region of the
+//     every lane owns one (KV head, slot) and reads that token's 16-byte
+//     pieces (FP8 codes, or BF16 keys: twice the pieces, half the pages) for
+//     all pages at once (a wavefront reads one contiguous run per piece),
+//     scores them, and the keys >= tau are compacted in position order
+//     straight from the ballot masks into the chunk's region of the
 //     candidate buffer; the chunk's count is recorded.
 //  3. finish    (one 1024-thread block per (sequence, KV head)): gathers the
 //     candidates into LDS in chunk order (so they are in position order),
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   const int ns = sp * a.P;
   // sample loads go out in two steps around the query work: the block-table
   // entries of every round first (with the query loads), then each round's
-  // FP8 rows (round 0 as soon as the query is summed).  Round r covers the
+  // scoring-cache rows (round 0 as soon as the query is summed).  Round r covers the
   // sample indices u = (r TPT + j) threads + tid, j < TPT.
   uint4 pc[TPT][RP];
   float sc[TPT];
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     for (int k = 0; k < 8; ++k) qpart[qgrp * din + qc * 8 + k] = acc[k];
   }
   // the query registers are free now: the sample pages go to LDS and round
-  // 0's FP8 rows go out (each thread reads back only its own sph entries)
+  // 0's rows go out (each thread reads back only its own sph entries)
   if (sampled) {
 #pragma unroll
     for (int k = 0; k < KS; ++k)
