@@ -218,6 +218,47 @@ def test_format_mla_store_and_select(fmt):
         check_selection(gidx[b, 0], oidx, sc, tau)
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_format_mla_decode_step(fmt):
+    """jssa_decode on MLA stores the new latent row in the format (fused into the select), selects and
+    attends."""
+    w = _w("tiny_mla", name="mla_mid", model="test", batch=2, seq_len=40000, budget=1024)
+    sfmt = L.SCALE_FORMATS[fmt]
+    shape = L.shape_for(w, scale_format=sfmt)
+    case = make_mla_case(w, ragged=True)
+    m32 = population_basis(w, 0, 0).astype(np.float32)
+    M = torch.from_numpy(m32).to(DEV)
+    kp, ks = _gpu_store(w, shape, case, M, case.latent)
+    bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
+    lat = bf16_bits(case.latent)
+    rows = [ogqa.logical_rows(lat, bt[b], int(sl[b]), w.page_size) for b in range(w.batch)]
+    new_slot = np.array([bt[b, (sl[b] - 1) // w.page_size] * w.page_size + (sl[b] - 1) % w.page_size
+                         for b in range(w.batch)], np.int32)
+    k_new = torch.from_numpy(np.stack([rows[b][-1] for b in range(w.batch)]).view(np.int16)).view(torch.bfloat16)
+    idx = torch.empty((w.batch, 1, w.budget), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+    kp_before = kp.clone()
+    ks_before = None if ks is None else ks.clone()
+    L.jssa_decode(shape, case.q.to(DEV), k_new.to(DEV), torch.from_numpy(new_slot).to(DEV), M, kp, ks,
+                  case.latent.to(DEV), None, case.block_table.to(DEV), case.seq_lens.to(DEV), idx, w.sm_scale, out,
+                  L.alloc_workspace(shape))
+    torch.cuda.synchronize()
+    assert torch.equal(kp, kp_before)                          # the fused store writes what jssa_store wrote
+    assert ks is None or torch.equal(ks, ks_before)
+    kp_h, ks_h = kp.cpu().numpy(), (None if ks is None else ks.cpu().numpy())
+    gidx, got = idx.cpu().numpy(), out.float().cpu().numpy()
+    q = bf16_bits(case.q)
+    for b in range(w.batch):
+        n = int(sl[b])
+        gc, gs = _unpack(kp_h, ks_h, bt[b], n, w.page_size, 0)
+        sc = ogqa.scores(omla.project_query(q[b], m32), gc, gs, fmt)
+        oidx, tau = ogqa.select_topb(sc, w.budget)
+        check_selection(gidx[b, 0], oidx, sc, tau)
+        sel = gidx[b, 0][gidx[b, 0] >= 0]
+        o, _ = omla.attend(q[b], rows[b][sel], w.sm_scale)
+        check_attention(got[b], o)
+
+
 def test_e8m0_hardware_bytes_match_the_definition():
     """Rows built so the fp32 scale is exactly a power of two, just above and just below one."""
     w = _w("tiny", name="pow2", model="test", batch=1, seq_len=64, budget=16)
