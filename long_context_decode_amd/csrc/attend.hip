@@ -9,20 +9,22 @@
 // Block = (split, KV head, sequence), 4 wavefronts; a wavefront takes 64
 // positions at a time ("batch"), lane i resolving position i to its K/V row
 // through the block table.  Row r of 16 lanes handles positions 16r..16r+15,
-// one per iteration; a lane holds D/16 contiguous elements of the row (one
-// 16-byte load for d = 128).  Per batch:
-//   A. the K rows are requested in groups of 8, then q.k is formed with
-//      v_dot2_f32_bf16 on the bf16 pairs and summed over the row with DPP;
-//      every position's logit (base 2, scaled by sm * log2 e) lands in the
-//      lane that owns the position;
+// one per iteration; a lane holds D/16 elements of the row, 8 contiguous ones
+// of each 128-dim block (one 16-byte load per block, so that a load
+// instruction covers 256 contiguous bytes of the row).  Per batch:
+//   A. the K rows are requested 16 (d = 128) or 8 (d = 256) at a time, then
+//      q.k is formed with v_dot2_f32_bf16 on the bf16 pairs and summed over
+//      the row with DPP; every position's logit (base 2, scaled by
+//      sm * log2 e) lands in the lane that owns the position;
 //   B. one softmax update per batch: the wave max of the 64 logits, a single
 //      rescale of the running state, p = 2^(x - m) per lane;
-//   C. the V rows are requested in groups of 8 and o += p v, p broadcast along
-//      the row with DPP (row_newbcast).
+//   C. the V rows are requested 8 (d = 128) or 4 (d = 256) at a time and
+//      o += p v, p broadcast along the row with DPP (row_newbcast).
 // Each loaded row serves all G query heads of the KV head.  The running max is
-// uniform over the wavefront, so the rows' partial sums add directly; waves
-// merge in LDS, splits in merge_kernel.  DENSE instantiates the full-KV /
-// sliding-window baseline (positions [lo, N) instead of an index list).
+// uniform over the wavefront, so the rows' partial sums add directly; each
+// wavefront writes its own partial (o, m, l), and merge_kernel combines them.
+// DENSE instantiates the full-KV / sliding-window baseline (positions [lo, N)
+// instead of an index list).
 #include "common.h"
 #include "kernels.h"
 
@@ -141,6 +143,16 @@ __global__ __launch_bounds__(256) void merge_kernel(AttendArgs a) {
   if (tid == 0 && a.lse_out) a.lse_out[(int64_t)b * a.Hq + j] = L > 0.0f ? (mm + log2f(L)) * kLn2 : -INFINITY;
 }
 
+// 16 bytes of a K or V row; the full-cache scan reads every row once, so its
+// loads are streaming (non-temporal) ones
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_row_piece(const uint16_t* p) {
+  return STREAM ? load_stream_u4(p) : *reinterpret_cast<const uint4*>(p);
+}
+
+// Lane (row, c16) of a wavefront holds dims 128 v + 8 c16 ... 128 v + 8 c16 + 7
+// (v < D / 128) of the query, the K and V rows and the output, so that each
+// 16-byte load instruction covers 256 contiguous bytes of a row.
 template <int D, int G, bool DENSE>
 __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   constexpr int EPL = D / 16;   // elements per lane
@@ -170,10 +182,10 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   uint32_t qp[G][NP];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint16_t* q = a.q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * D + c16 * EPL;
+    const uint16_t* q = a.q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * D + c16 * 8;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const uint4 u = *reinterpret_cast<const uint4*>(q + v * 8);
+      const uint4 u = *reinterpret_cast<const uint4*>(q + v * 128);
       qp[g][4 * v] = u.x;
       qp[g][4 * v + 1] = u.y;
       qp[g][4 * v + 2] = u.z;
@@ -190,8 +202,8 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   }
 
   const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive token slots
-  const uint16_t* kbase = a.k_cache + (int64_t)h * D + c16 * EPL;
-  const uint16_t* vbase = a.v_cache + (int64_t)h * D + c16 * EPL;
+  const uint16_t* kbase = a.k_cache + (int64_t)h * D + c16 * 8;
+  const uint16_t* vbase = a.v_cache + (int64_t)h * D + c16 * 8;
   const int32_t* idx = DENSE ? nullptr : a.indices + ((int64_t)b * a.Hkv + h) * a.B;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
         const int rr = row_bcast(ri, u0 + u);
         const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) kr[u][v] = *reinterpret_cast<const uint4*>(kbase + ro + v * 8);
+        for (int v = 0; v < NV; ++v) kr[u][v] = load_row_piece<DENSE>(kbase + ro + v * 128);
       }
 #pragma unroll
       for (int u = 0; u < GRPK; ++u) {
@@ -264,7 +276,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
         const int rr = row_bcast(ri, u0 + u);
         const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) vr[u][v] = *reinterpret_cast<const uint4*>(vbase + ro + v * 8);
+        for (int v = 0; v < NV; ++v) vr[u][v] = load_row_piece<DENSE>(vbase + ro + v * 128);
       }
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {
@@ -307,7 +319,7 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
     if (row == 0) {
 #pragma unroll
       for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<float4*>(&a.part_o[pj * D + c16 * EPL + e]) =
+        *reinterpret_cast<float4*>(&a.part_o[pj * D + (e >> 3) * 128 + c16 * 8 + (e & 7)]) =
             make_float4(o[g][e], o[g][e + 1], o[g][e + 2], o[g][e + 3]);
       if (c16 == 0) {
         a.part_ml[pj * 2] = m[g];

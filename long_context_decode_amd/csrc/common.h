@@ -9,6 +9,20 @@ namespace jssa {
 constexpr int kWave = 64;
 
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- streaming loads
+
+// Loads of data that one step reads exactly once (the scoring cache in the
+// score stream): marked non-temporal, so that they do not displace what the
+// caches hold for later reads.
+__device__ __forceinline__ uint4 load_stream_u4(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t load_stream_u32(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
+}
 
 // ---------------------------------------------------------------- bf16
 
@@ -116,12 +130,24 @@ __device__ __forceinline__ void store_scale(void* base, int64_t i, int sfmt, uin
 // scale, BF16 keys).
 // (E8M0 scale arrays start 4-byte aligned; the word of element i lies inside
 // the array because the page size is a multiple of 4.)
+// E8M0 byte E -> 2^(E - 127) (E = 0: 2^-127, a subnormal fp32)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? (e << 23) : 0x00400000u); }
+
 __device__ __forceinline__ float load_scale(const void* base, int64_t i, int sfmt) {
   if (sfmt == 0) return static_cast<const float*>(base)[i];
   if (sfmt == 1) {       // the aligned word holding the byte (four lanes share one load)
     const uint32_t w = static_cast<const uint32_t*>(base)[i >> 2];
-    const uint32_t b = (w >> ((i & 3) * 8)) & 0xffu;
-    return __uint_as_float(b ? (b << 23) : 0x00400000u);
+    return e8m0_to_f32((w >> ((i & 3) * 8)) & 0xffu);
+  }
+  return 1.0f;
+}
+
+// load_scale with streaming (non-temporal) loads
+__device__ __forceinline__ float load_scale_stream(const void* base, int64_t i, int sfmt) {
+  if (sfmt == 0) return __uint_as_float(load_stream_u32(static_cast<const uint32_t*>(base) + i));
+  if (sfmt == 1) {
+    const uint32_t w = load_stream_u32(static_cast<const uint32_t*>(base) + (i >> 2));
+    return e8m0_to_f32((w >> ((i & 3) * 8)) & 0xffu);
   }
   return 1.0f;
 }

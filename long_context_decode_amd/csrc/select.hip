@@ -165,14 +165,15 @@ __device__ __forceinline__ void load_token(const SelectArgs& a, int64_t phys, in
   sc = load_scale(a.kp_scale, (phys * a.Hkv + head) * a.P + slot, a.sfmt);
 }
 
-// load_token with the scale format fixed at compile time (the stream kernel).
+// load_token for the stream kernel: the scale format fixed at compile time,
+// and streaming loads (each byte of the scoring cache is read once per step)
 template <int R, int SF>
 __device__ __forceinline__ void load_token_sf(const SelectArgs& a, int64_t phys, int head, int slot, uint4 (&pc)[R],
                                               float& sc) {
   const uint8_t* base = a.kp + (phys * a.Hkv + head) * ((int64_t)R * 16 * a.P) + slot * 16;
 #pragma unroll
-  for (int j = 0; j < R; ++j) pc[j] = *reinterpret_cast<const uint4*>(base + (int64_t)j * a.P * 16);
-  sc = load_scale(a.kp_scale, (phys * a.Hkv + head) * a.P + slot, SF);
+  for (int j = 0; j < R; ++j) pc[j] = load_stream_u4(base + (int64_t)j * a.P * 16);
+  sc = load_scale_stream(a.kp_scale, (phys * a.Hkv + head) * a.P + slot, SF);
 }
 
 template <int R, bool BF>
