@@ -162,6 +162,13 @@ class Layer:
         self.__dict__.update(kw)
 
 
+def fused_applies(w) -> bool:
+    """Whether jssa_decode's AUTO mode takes the single-launch path for this workload (the library's rule:
+    GQA, r <= 64, G * d <= 512, sequence capacity <= 12288 tokens, B <= 4096)."""
+    return (w.kind == "gqa" and w.rank <= 64 and w.head_dim in (128, 256) and w.group in (1, 2, 4)
+            and w.group * w.head_dim <= 512 and w.pages_per_seq * w.page_size <= 12288 and w.budget <= 4096)
+
+
 def setup(w, device, replicas, scale_format="fp32"):
     """Returns (shape, layers of every replica, block_table, seq_lens, generated case)."""
     import torch
@@ -511,6 +518,8 @@ def main():
     ap.add_argument("--scale-format", default="fp32", choices=["fp32", "e8m0", "none", "bf16"],
                     help="scoring-cache format: FP8 with an fp32 scale per token (default), with a one-byte power of two, "
                          "with no scale, or BF16 projected keys")
+    ap.add_argument("--decode-path", default="auto", choices=["auto", "split", "fused"],
+                    help="jssa_decode's path: the library's choice, the five-launch split path, or the single launch")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reference for counter scaling)")
     ap.add_argument("--recall-sweep", action="store_true",
@@ -572,12 +581,15 @@ def main():
     ws = L.alloc_workspace(shape, dev)
     idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=dev)
     out = torch.empty((w.batch, w.num_q_heads, w.v_dim), dtype=torch.bfloat16, device=dev)
+    modes = {"auto": L.SELECT_AUTO, "split": L.SELECT_SPLIT, "fused": L.SELECT_FUSED}
+    single = fused_applies(w) if args.decode_path == "auto" else args.decode_path == "fused"
 
-    def run_layer(lay, sparse):
+    def run_layer(lay, sparse, mode=modes[args.decode_path]):
         if lay.window or not sparse:
             L.jssa_full_decode(shape, lay.q, lay.kc, lay.vc, bt, sl, lay.window, w.sm_scale, out, ws)
         else:
-            L.jssa_decode(shape, lay.q, lay.k_new, lay.slot_new, lay.M, lay.kp, lay.ks, lay.kc, lay.vc, bt, sl,
+            dshape = L.shape_for(w, scale_format=L.SCALE_FORMATS[args.scale_format], select_mode=mode)
+            L.jssa_decode(dshape, lay.q, lay.k_new, lay.slot_new, lay.M, lay.kp, lay.ks, lay.kc, lay.vc, bt, sl,
                           idx, w.sm_scale, out, ws)
 
     def step(r):
@@ -598,6 +610,15 @@ def main():
         print(f"[bench] graph {g_ms:.4f} ms/step", file=sys.stderr, flush=True)
     ms_full, _, _, _, _ = time_steps(full, max(10, args.steps // 10), max(2, args.warmup // 4), n_rep)
     print(f"[bench] full-KV {ms_full:.4f} ms/step", file=sys.stderr, flush=True)
+    paths = None
+    if single:                                  # the same step through the five-launch split path
+        def split_step(r):
+            for lay in reps[r]:
+                run_layer(lay, True, L.SELECT_SPLIT)
+        ms_split = time_steps(split_step, args.steps, args.warmup, n_rep)[0]
+        paths = {"single_launch_ms": round(ms, 5), "split_ms": round(ms_split, 5),
+                 "ratio": round(ms_split / ms, 3)}
+        print(f"[bench] split path {ms_split:.4f} ms/step", file=sys.stderr, flush=True)
 
     # stages of the sparse layers, rotating over (replica, layer) so that no launch finds the previous
     # launch's bytes in the Infinity Cache (and the whole of a window layer, if any)
@@ -672,7 +693,8 @@ def main():
            "budget": w.budget, "kv_dtype": "bf16",
            "scoring_cache": {"fp32": "fp8 e4m3fn + fp32 scale per token", "e8m0": "fp8 e4m3fn + e8m0 scale byte",
                              "none": "fp8 e4m3fn, no scale", "bf16": "bf16 projected keys, no scale"}[args.scale_format],
-           "replicas": n_rep}
+           "replicas": n_rep,
+           "decode_path": "single launch per layer" if single else "split (prologue, stream, finish, attend, merge)"}
     if w.window:
         cfg.update(layers=w.num_layers, window=w.window, window_layers=list(w.window_layers()))
     res = {
@@ -697,6 +719,7 @@ def main():
         "bytes_breakdown": parts,
         "block_median_ms": round(med, 5), "p10_ms": round(p10, 5), "p90_ms": round(p90, 5),
         "graph": graph,
+        "decode_paths": paths,
         "hbm_copy_probe_gbps": round(2 * PROBE_BYTES / (probe_ms * 1e-3) / 1e9, 1),
         "full_kv_ms_per_step": round(ms_full, 4),
         "full_kv_gbps": round(full_bytes / (ms_full * 1e-3) / 1e9, 1),

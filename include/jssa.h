@@ -77,14 +77,29 @@ typedef enum {
 
 enum { JSSA_KIND_GQA = 0, JSSA_KIND_MLA = 1 };
 
-/* jssa_select strategies (both return the same set):
- *   AUTO          sampled threshold + candidate compaction in one pass over the
- *                 FP8 cache, exact top-B of the candidates in LDS; falls back to
- *                 EXACT_STREAM per (sequence, KV head) whenever the candidate
- *                 set could miss a member of the top-B.
+/* jssa_shape.select_mode: the selection strategy, and the path jssa_decode
+ * takes.  Every mode returns the same index set and the same scores.
+ *   AUTO          jssa_select: sampled threshold + candidate compaction in one
+ *                 pass over the scoring cache, exact top-B of the candidates in
+ *                 LDS; falls back to EXACT_STREAM per (sequence, KV head)
+ *                 whenever the candidate set could miss a member of the top-B.
+ *                 jssa_decode: the single-launch path (FUSED) when the shape
+ *                 allows it, else SPLIT.
  *   EXACT_STREAM  per (sequence, KV head) radix select over recomputed scores
- *                 (several passes over the FP8 cache; slow, data independent). */
-enum { JSSA_SELECT_AUTO = 0, JSSA_SELECT_EXACT_STREAM = 1 };
+ *                 (several passes over the scoring cache; slow, data
+ *                 independent); jssa_decode takes the split path.
+ *   SPLIT         as AUTO, but jssa_decode always takes the split path: select
+ *                 prologue, score stream and finish, then split-K attention and
+ *                 merge (five launches per layer).
+ *   FUSED         jssa_decode in one launch per layer (summary page §3.3: one
+ *                 launch per layer): one block per (sequence, KV head) forms
+ *                 qhat, stores the new token, scores every position exactly
+ *                 into on-chip memory, selects the top-B and attends.  Only for
+ *                 GQA with max_pages_per_seq * page_size <= 12288, rank <= 64
+ *                 and G * head_dim <= 512; jssa_decode returns
+ *                 JSSA_ERR_UNSUPPORTED for other shapes.  jssa_select treats
+ *                 SPLIT and FUSED as AUTO. */
+enum { JSSA_SELECT_AUTO = 0, JSSA_SELECT_EXACT_STREAM = 1, JSSA_SELECT_SPLIT = 2, JSSA_SELECT_FUSED = 3 };
 
 /* jssa_shape.scale_format: the scoring cache's format, FP8 codes with a
  * per-(token, KV head) scale of one of three kinds, or BF16 keys. */
@@ -100,7 +115,7 @@ typedef struct jssa_shape {
   int32_t max_pages_per_seq;  /* row stride of block_table */
   int32_t rank;               /* r: GQA r % 16 == 0, r <= min(d, 128); MLA latent rank, 64 */
   int32_t budget;             /* B: 1..4096 */
-  int32_t select_mode;        /* JSSA_SELECT_AUTO or JSSA_SELECT_EXACT_STREAM */
+  int32_t select_mode;        /* JSSA_SELECT_AUTO, _EXACT_STREAM, _SPLIT or _FUSED */
   int32_t scale_format;       /* JSSA_SCALE_FP32 (0), JSSA_SCALE_E8M0, JSSA_SCALE_NONE or JSSA_KEYS_BF16 */
 } jssa_shape;
 
@@ -180,7 +195,9 @@ int32_t jssa_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
 /* jssa_decode — one decode step: [jssa_store of k_new at slot_new, skipped when
  * k_new is NULL] -> jssa_select -> jssa_attend, all on `stream`.  k_new holds
  * one new key per sequence (T = batch), i.e. the token at position
- * seq_lens[b]-1, so the token being decoded is itself eligible for selection. */
+ * seq_lens[b]-1, so the token being decoded is itself eligible for selection.
+ * The results equal those of the three calls; shape->select_mode picks the
+ * split path (five launches) or the single-launch one (see JSSA_SELECT_FUSED). */
 int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_new,
                     const int32_t* slot_new, const float* M, uint8_t* kp, void* kp_scale,
                     const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* block_table,

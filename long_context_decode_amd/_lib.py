@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libjssa.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 KIND_GQA, KIND_MLA = 0, 1
-SELECT_AUTO, SELECT_EXACT_STREAM = 0, 1
+SELECT_AUTO, SELECT_EXACT_STREAM, SELECT_SPLIT, SELECT_FUSED = 0, 1, 2, 3
 SCALE_FP32, SCALE_E8M0, SCALE_NONE, KEYS_BF16 = 0, 1, 2, 3
 SCALE_FORMATS = {"fp32": SCALE_FP32, "e8m0": SCALE_E8M0, "none": SCALE_NONE, "bf16": KEYS_BF16}
 STAGE_PROLOGUE, STAGE_STREAM, STAGE_FINISH, STAGE_ALL = 1, 2, 4, 7

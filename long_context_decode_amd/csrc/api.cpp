@@ -61,6 +61,8 @@ void mla_dense_plan(int64_t n, int batch, int Hq, int* splits, int* len) {
   *splits = (int)cdiv(n, *len);
 }
 
+constexpr float kLog2e = 1.44269504088896340736f;
+
 // formats without a scale array
 bool scale_free(int sfmt) { return sfmt == JSSA_SCALE_NONE || sfmt == JSSA_KEYS_BF16; }
 
@@ -72,7 +74,7 @@ int32_t validate_shape(const jssa_shape* sh) {
   if (sh->num_q_heads % sh->num_kv_heads != 0) return JSSA_ERR_SHAPE;
   if (sh->budget < 1 || sh->budget > 4096) return JSSA_ERR_SHAPE;
   if (sh->page_size != 16 && sh->page_size != 32 && sh->page_size != 64) return JSSA_ERR_UNSUPPORTED;
-  if (sh->select_mode != JSSA_SELECT_AUTO && sh->select_mode != JSSA_SELECT_EXACT_STREAM) return JSSA_ERR_SHAPE;
+  if (sh->select_mode < JSSA_SELECT_AUTO || sh->select_mode > JSSA_SELECT_FUSED) return JSSA_ERR_SHAPE;
   if (sh->scale_format != JSSA_SCALE_FP32 && sh->scale_format != JSSA_SCALE_E8M0 &&
       sh->scale_format != JSSA_SCALE_NONE && sh->scale_format != JSSA_KEYS_BF16)
     return JSSA_ERR_UNSUPPORTED;
@@ -238,7 +240,7 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
   a.part_ml = at<float>(ws, p.off_part_ml);
   a.out = out;
   a.lse_out = lse_out;
-  a.sm_log2 = sm_scale * 1.44269504088896340736f;
+  a.sm_log2 = sm_scale * kLog2e;
   a.batch = p.batch;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
@@ -365,6 +367,38 @@ int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
   if (!p.mla && !v_cache) return JSSA_ERR_NULL;
   if (k_new && !slot_new) return JSSA_ERR_NULL;
   if (workspace_bytes < p.total) return JSSA_ERR_WORKSPACE;
+  const int mode = shape->select_mode;
+  const bool fits = fused_applies(p.mla, p.d, p.G, p.r, p.maxN, p.B);
+  if (mode == JSSA_SELECT_FUSED && !fits) return JSSA_ERR_UNSUPPORTED;
+  if (mode == JSSA_SELECT_FUSED || (mode == JSSA_SELECT_AUTO && fits)) {
+    FusedArgs f{};
+    f.q = q;
+    f.k_new = k_new;
+    f.slot_new = k_new ? slot_new : nullptr;
+    f.M = M;
+    f.kp = kp;
+    f.kp_scale = kp_scale;
+    f.k_cache = k_cache;
+    f.v_cache = v_cache;
+    f.block_table = block_table;
+    f.seq_lens = seq_lens;
+    f.indices = indices;
+    f.out = out;
+    f.lse_out = lse_out;
+    f.sm_log2 = sm_scale * kLog2e;
+    f.batch = p.batch;
+    f.Hq = p.Hq;
+    f.Hkv = p.Hkv;
+    f.d = p.d;
+    f.P = p.P;
+    f.max_pages = p.max_pages;
+    f.r = p.r;
+    f.S = p.S;
+    f.B = p.B;
+    f.G = p.G;
+    f.sfmt = p.sfmt;
+    return hip_status(launch_fused(f, stream));
+  }
   // the prologue of select stores the new token
   st = do_select(p, shape->select_mode, JSSA_STAGE_ALL, q, M, kp, kp_scale, block_table, seq_lens, indices, nullptr,
                  workspace, workspace_bytes, stream, k_new, k_new ? slot_new : nullptr);

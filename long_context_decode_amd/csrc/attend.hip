@@ -37,18 +37,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 }  // namespace
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 // Combine the splits of every (sequence, query head): o = sum_s 2^(m_s - m*) o_s /
 // sum_s 2^(m_s - m*) l_s, lse = ln 2 * (m* + log2 sum_s 2^(m_s - m*) l_s).
 // One block per (query head, sequence).  Every load goes out first: thread s

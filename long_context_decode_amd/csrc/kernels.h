@@ -64,6 +64,28 @@ struct AttendArgs {
   int parts;               // partials per split: 4 (one per wavefront, GQA) or 1 (MLA)
 };
 
+// jssa_decode in one launch (fused.hip): one block per (sequence, KV head)
+constexpr int kFusedMaxB = 4096;      // selected positions the block holds in LDS
+
+struct FusedArgs {
+  const uint16_t* q;
+  const uint16_t* k_new;   // NULL: no new token
+  const int32_t* slot_new;
+  const float* M;
+  uint8_t* kp;
+  void* kp_scale;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t* indices;
+  uint16_t* out;
+  float* lse_out;
+  float sm_log2;
+  int batch, Hq, Hkv, d, P, max_pages, r, S, B, G;
+  int sfmt;
+};
+
 struct GatherArgs {
   const uint16_t* k_cache;
   const uint16_t* v_cache;   // NULL for MLA (one latent row)
@@ -94,6 +116,9 @@ hipError_t launch_mla_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttendArgs& a, int dv, hipStream_t s);
 hipError_t launch_calib(const CalibArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
+// whether the single-launch decode handles this shape (capacity = max_pages * P)
+bool fused_applies(int mla, int d, int G, int r, int64_t capacity, int B);
 
 // host: per-head top-r eigenvectors of the unit-trace-normalised moment sum
 int32_t basis_impl(int hkv, int n, int r, const float* gq, const float* gk, float* m_out);

@@ -27,6 +27,7 @@
 //     token of the sequence itself (same scoring function, same bits).
 #include "common.h"
 #include "kernels.h"
+#include "radix.h"
 
 namespace jssa {
 
@@ -35,123 +36,6 @@ namespace {
 constexpr int kPrologueThreads = 1024;
 constexpr int kFinishThreads = 1024;
 constexpr int kStreamThreads = 256;
-
-// ------------------------------------------------------------------ radix select
-
-constexpr int kDigitBits = 11;
-constexpr int kBins = 1 << kDigitBits;
-
-// Histogram bins are stored transposed with one word of padding per row: bin d
-// at word (d % 32) * 65 + d / 32.  Lane l of a wavefront then reads "its" 32
-// consecutive bins [32l, 32l + 32) with reads that are consecutive across
-// lanes, and neighbouring bins (where keys cluster) sit in different banks.
-constexpr int kHistWords = 32 * 65;
-__device__ __forceinline__ uint32_t bin_slot(uint32_t d) { return (d & 31u) * 65u + (d >> 5); }
-
-// Pick the digit d of the current pass so that fewer than k matching keys have
-// a larger digit and at least k have a digit >= d: thread t owns kBins/NT
-// consecutive bins; the count above its bins comes from a block prefix sum.
-// (Used by the exact re-scoring path, where the whole block streams tokens.)
-template <int NT>
-__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t k, uint32_t* tmp, uint32_t* bcast) {
-  constexpr int BPT = kBins / NT;
-  const int tid = (int)threadIdx.x;
-  uint32_t c[BPT], s = 0;
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    c[j] = hist[bin_slot((uint32_t)(tid * BPT + j))];
-    s += c[j];
-  }
-  uint32_t total;
-  const uint32_t ex = block_excl_scan<NT>(s, tmp, &total);
-  uint32_t above = total - ex - s;  // keys in the bins of higher threads
-#pragma unroll
-  for (int j = BPT - 1; j >= 0; --j) {
-    if (above < k && k <= above + c[j]) {
-      bcast[0] = (uint32_t)(tid * BPT + j);
-      bcast[1] = k - above;
-    }
-    above += c[j];
-  }
-}
-
-
-// Wave 0 only: find the digit d with count(digit > d) < k <= count(digit >= d)
-// and publish d and k - count(digit > d) in bcast[0..1].
-__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k, uint32_t* bcast) {
-  const int l = lane_id();
-  uint32_t sum = 0;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) sum += hist[j * 65 + l];
-  const uint32_t pre = wave_incl_scan(sum);
-  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63);
-  const uint32_t suf = total - pre + sum;  // inclusive suffix sum over lanes >= l
-  const uint32_t above = suf - sum;
-  // the lane whose 32 bins hold the k-th key, then the bin among those 32,
-  // with lanes 0..31 taking one bin each (uniform control flow)
-  const int ls = (int)__builtin_ctzll(ballot(above < k && k <= suf));
-  const uint32_t above_ls = (uint32_t)__builtin_amdgcn_readlane((int)above, ls);
-  const uint32_t tot_ls = (uint32_t)__builtin_amdgcn_readlane((int)sum, ls);
-  const uint32_t cj = l < 32 ? hist[l * 65 + ls] : 0u;
-  const uint32_t pj = wave_incl_scan(cj);
-  const uint32_t incl = above_ls + (tot_ls - pj + cj), excl = incl - cj;
-  const bool hit = l < 32 && excl < k && k <= incl;
-  const int js = (int)__builtin_ctzll(ballot(hit));
-  if (l == js) {
-    bcast[0] = (uint32_t)(ls * 32 + js);
-    bcast[1] = k - excl;
-  }
-}
-
-// k-th largest key (1-based) of keys[0..n) in LDS and how many keys equal to it
-// belong to the top k.  Skips the leading bits all keys share, then resolves
-// kDigitBits bits per pass: every thread adds its keys to an LDS histogram,
-// wave 0 finds the digit; two block barriers per pass (the histogram of the
-// next pass is cleared during the current one).  hist2 holds 2 * kHistWords words.
-//
-// With stop_shift > 0 the digits below bit stop_shift are not resolved: *kth
-// is then the lower edge (low bits zero) of the bin holding the k-th key, a
-// bound <= the k-th key, and *need is not meaningful.
-template <int NT>
-__device__ void block_radix_select(const uint32_t* keys, int n, uint32_t k, uint32_t* hist2, uint32_t* tmp,
-                                   uint32_t* kth, uint32_t* need, int stop_shift = 0) {
-  const int tid = (int)threadIdx.x;
-  for (int i = tid; i < kHistWords; i += NT) hist2[i] = 0u;
-  const uint32_t ref = keys[0];
-  uint32_t orv = 0;
-  for (int i = tid; i < n; i += NT) orv |= keys[i] ^ ref;
-  orv = block_or<NT>(orv, tmp);       // barriers also publish the cleared histogram
-  if (orv == 0u) {
-    *kth = ref;
-    *need = k;
-    return;
-  }
-  int hb = 31 - __builtin_clz(orv);
-  uint32_t hi_mask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
-  uint32_t prefix = ref & hi_mask;
-  for (int pass = 0;; ++pass) {
-    uint32_t* cur = hist2 + (pass & 1) * kHistWords;
-    uint32_t* nxt = hist2 + ((pass + 1) & 1) * kHistWords;
-    const int shift = hb >= kDigitBits - 1 ? hb - (kDigitBits - 1) : 0;
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t key = keys[i];
-      if ((key & hi_mask) == prefix) atomicAdd(&cur[bin_slot((key >> shift) & (kBins - 1u))], 1u);
-    }
-    for (int i = tid; i < kHistWords; i += NT) nxt[i] = 0u;
-    __syncthreads();
-    if (tid < 64) wave_find_digit(cur, k, tmp + 48);
-    __syncthreads();
-    prefix = (prefix & ~((kBins - 1u) << shift)) | (tmp[48] << shift);
-    k = tmp[49];
-    hi_mask = ~((1u << shift) - 1u);
-    prefix &= hi_mask;
-    if (shift <= stop_shift) break;
-    hb = shift - 1;
-  }
-  *kth = prefix;
-  *need = k;
-  __syncthreads();                     // tmp is reused by the caller
-}
 
 // ------------------------------------------------------------------ token access
 
@@ -239,10 +123,12 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   const int nf = dm / 32;                      // float4 groups per thread: 4, 8 or 16
   const bool mpre = nf <= 4 && mo < a.r;
   float4 mpv[4];
-  if (mpre) {
-    const float* m = Mh + (int64_t)mo * dm + mpart * 4;
+  {
+    // unconditional loads from a clamped row (dims < 128 <= dm), so that no
+    // branch join waits for them
+    const float* m = Mh + (int64_t)(mo < a.r ? mo : 0) * dm + mpart * 4;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) mpv[k] = k < nf ? *reinterpret_cast<const float4*>(m + k * 32) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < 4; ++k) mpv[k] = *reinterpret_cast<const float4*>(m + k * 32);
   }
 
   // sample plan: a strided set of whole pages; tau will be the ks-th largest
@@ -266,7 +152,10 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   // sample loads go out in two steps around the query work: the block-table
   // entries of every round first (with the query loads), then each round's
   // scoring-cache rows (round 0 as soon as the query is summed).  Round r covers the
-  // sample indices u = (r TPT + j) threads + tid, j < TPT.
+  // sample indices u = (r TPT + j) threads + tid, j < TPT.  P (16, 32 or 64)
+  // divides the thread count, so every index of this thread has slot tid mod P.
+  const int lp = 31 - __builtin_clz(a.P);
+  const int sslot = tid & (a.P - 1);
   uint4 pc[TPT][RP];
   float sc[TPT];
   constexpr int KS = kSampleMax / kPrologueThreads;
@@ -275,18 +164,22 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       const int u = k * kPrologueThreads + tid;
-      ph[k] = -1;
-      if (u < ns) {
-        const int pl = (int)(((int64_t)(u / a.P) * n_pages) / sp);
-        if (pl * a.P + u % a.P < N) ph[k] = a.block_table[(int64_t)b * a.max_pages + pl];
-      }
+      // sample page i -> logical page floor(i n_pages / sp); exact in fp64
+      // (i n_pages < 2^53, and a quotient that is not an integer lies at
+      // least 1/sp below the next one)
+      const int pl = (int)(((double)(u >> lp) * (double)n_pages) / (double)sp);
+      const bool ok = u < ns && pl * a.P + sslot < N;
+      // unconditional (clamped) loads: no branch join waits for them
+      const int e = a.block_table[(int64_t)b * a.max_pages + (ok ? pl : 0)];
+      ph[k] = ok ? e : -1;
     }
   }
   auto issue_rows = [&](int r) {
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
       const int u = (r * TPT + j) * kPrologueThreads + tid;
-      if (u < ns && sph[u] >= 0) load_token<RP>(a, sph[u], h, u % a.P, pc[j], sc[j]);
+      const int pg = u < ns ? sph[u] : -1;
+      load_token<RP>(a, pg >= 0 ? pg : 0, h, sslot, pc[j], sc[j]);
     }
   };
 
@@ -628,9 +521,9 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   }
   if (tid == 0) coff[n_chunks] = carry;
   __syncthreads();
-  // gather the candidates in position order: thread c copies chunk c's
-  // contiguous run to its offset; the first 16 entries are read
-  // unconditionally (prefetched for c = tid), the rest, if any, one by one
+  // gather the candidates in position order: thread c copies the first 16
+  // entries of chunk c's contiguous run to its offset (read unconditionally,
+  // prefetched for c = tid)
   {
     for (int c = tid; c < n_chunks; c += kFinishThreads) {
       const int cnt = (int)(coff[c + 1] - coff[c]);
@@ -655,10 +548,28 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
           lidx[dst + 2 * j + 1] = (int32_t)v[j].w;
         }
       }
-      for (int i = 16; i < cnt; ++i) {
-        const uint2 e = src[i];
-        lkey[dst + i] = e.x;
-        lidx[dst + i] = (int32_t)e.y;
+    }
+    // the rest: lpc lanes per chunk (more when the chunks are few), each lane
+    // with four clamped loads in flight, so that a tail of up to 4 lpc
+    // entries costs one round trip
+    const int w = tid >> 6, lane = tid & 63;
+    const int lpc = n_chunks >= 256 ? 4 : (n_chunks >= 64 ? 16 : 64);
+    const int cpw = 64 / lpc, sub = lane % lpc;
+    for (int c = w * cpw + lane / lpc; c < n_chunks; c += (kFinishThreads / 64) * cpw) {
+      const int cnt = (int)(coff[c + 1] - coff[c]);
+      const uint2* src = a.cand + (bh * a.max_chunks + c) * (int64_t)cap_chunk;
+      const uint32_t dst = coff[c];
+      for (int i0 = 16 + sub; i0 < cnt; i0 += 4 * lpc) {
+        uint2 e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) e[k] = src[i0 + k * lpc < cnt ? i0 + k * lpc : i0];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (i0 + k * lpc < cnt) {
+            lkey[dst + i0 + k * lpc] = e[k].x;
+            lidx[dst + i0 + k * lpc] = (int32_t)e[k].y;
+          }
+        }
       }
     }
   }

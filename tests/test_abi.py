@@ -44,7 +44,8 @@ def _shape(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=30), -2), (dict(budget=0), -2), (dict(budget=5000), -2), (dict(batch=0), -2),
     (dict(head_dim=64), -3), (dict(page_size=8), -3), (dict(rank=24), -3), (dict(rank=256, head_dim=256), -3),
-    (dict(num_q_heads=48), -3), (dict(kind=7), -3), (dict(select_mode=3), -2),
+    (dict(num_q_heads=48), -3), (dict(kind=7), -3), (dict(select_mode=4), -2), (dict(select_mode=-1), -2),
+    (dict(select_mode=3), 0),
     (dict(kind=1, num_kv_heads=2, num_q_heads=128, head_dim=576, rank=64), -3),
     (dict(kind=1, num_kv_heads=1, num_q_heads=128, head_dim=576, rank=64, page_size=64), 0),
 ])
@@ -88,6 +89,10 @@ def test_entry_points_reject_before_launch():
     assert lib.jssa_gather_attend(ref, fake, fake, fake, fake, fake, fake, 0.1, fake, nul, fake, 16, nul) == -4
     assert lib.jssa_decode(ref, fake, fake, nul, fake, fake, fake, fake, fake, fake, fake, fake, 0.1, fake, nul,
                            fake, 1 << 40, nul) == -1
+    # the single-launch path refuses shapes it does not cover (capacity 131072 > 12288), before any launch
+    fused = _shape(select_mode=L.SELECT_FUSED)
+    assert lib.jssa_decode(ctypes.byref(fused), fake, nul, nul, fake, fake, fake, fake, fake, fake, fake, fake, 0.1,
+                           fake, nul, fake, 1 << 40, nul) == -3
     assert lib.jssa_store(ref, nul, fake, 4, fake, fake, fake, nul) == -1
     assert lib.jssa_store(ref, fake, fake, -1, fake, fake, fake, nul) == -2
     assert lib.jssa_store(ref, nul, nul, 0, nul, nul, nul, nul) == 0          # T = 0: nothing to do
