@@ -162,13 +162,6 @@ class Layer:
         self.__dict__.update(kw)
 
 
-def fused_applies(w) -> bool:
-    """Whether jssa_decode's AUTO mode takes the single-launch path for this workload (the library's rule:
-    GQA, r <= 64, G * d <= 512, sequence capacity <= 12288 tokens, B <= 4096)."""
-    return (w.kind == "gqa" and w.rank <= 64 and w.head_dim in (128, 256) and w.group in (1, 2, 4)
-            and w.group * w.head_dim <= 512 and w.pages_per_seq * w.page_size <= 12288 and w.budget <= 4096)
-
-
 def setup(w, device, replicas, scale_format="fp32"):
     """Returns (shape, layers of every replica, block_table, seq_lens, generated case)."""
     import torch
@@ -582,7 +575,8 @@ def main():
     idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=dev)
     out = torch.empty((w.batch, w.num_q_heads, w.v_dim), dtype=torch.bfloat16, device=dev)
     modes = {"auto": L.SELECT_AUTO, "split": L.SELECT_SPLIT, "fused": L.SELECT_FUSED}
-    single = fused_applies(w) if args.decode_path == "auto" else args.decode_path == "fused"
+    single = L.decode_single_launch(L.shape_for(w, scale_format=L.SCALE_FORMATS[args.scale_format],
+                                                select_mode=modes[args.decode_path]))
 
     def run_layer(lay, sparse, mode=modes[args.decode_path]):
         if lay.window or not sparse:

@@ -127,6 +127,13 @@ const char* jssa_status_string(int32_t status);
  * page_size).  Writes *bytes; returns a jssa_status. */
 int32_t jssa_workspace_bytes(const jssa_shape* shape, size_t* bytes);
 
+/* Whether jssa_decode with this shape runs as one launch per layer (*single = 1:
+ * JSSA_SELECT_FUSED, or JSSA_SELECT_AUTO on a shape the single launch covers)
+ * or through the split path (*single = 0).  Returns JSSA_ERR_UNSUPPORTED for
+ * JSSA_SELECT_FUSED on a shape the single launch does not cover, as
+ * jssa_decode would. */
+int32_t jssa_decode_path(const jssa_shape* shape, int32_t* single);
+
 /* Bytes of the projected scoring cache per page (kp) and scale elements per
  * page (kp_scale: fp32 for JSSA_SCALE_FP32, bytes for JSSA_SCALE_E8M0, 0 for
  * JSSA_SCALE_NONE and JSSA_KEYS_BF16), so callers can size both buffers. */

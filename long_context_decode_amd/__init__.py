@@ -7,7 +7,8 @@ from ._lib import (  # noqa: F401
     KIND_GQA, KIND_MLA, SELECT_AUTO, SELECT_EXACT_STREAM, SELECT_SPLIT, SELECT_FUSED,
     STAGE_PROLOGUE, STAGE_STREAM, STAGE_FINISH, STAGE_ALL,
     SCALE_FP32, SCALE_E8M0, SCALE_NONE, KEYS_BF16, SCALE_FORMATS, MLA_LATENT, MLA_ROPE, EXPORTED, LIB_PATH,
-    JSSAError, Shape, make_shape, shape_for, status_string, workspace_bytes, kp_page_bytes, alloc_workspace,
+    JSSAError, Shape, make_shape, shape_for, status_string, workspace_bytes, decode_single_launch, kp_page_bytes,
+    alloc_workspace,
     alloc_scoring_cache, jssa_store, jssa_select, jssa_attend, jssa_decode, jssa_full_decode, jssa_gather_attend,
     calib_workspace_bytes, jssa_calib_moments, jssa_basis, raw_library,
 )

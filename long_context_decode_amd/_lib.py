@@ -26,7 +26,8 @@ SCALE_FORMATS = {"fp32": SCALE_FP32, "e8m0": SCALE_E8M0, "none": SCALE_NONE, "bf
 STAGE_PROLOGUE, STAGE_STREAM, STAGE_FINISH, STAGE_ALL = 1, 2, 4, 7
 MLA_LATENT, MLA_ROPE = 512, 64
 
-EXPORTED = ("jssa_status_string", "jssa_workspace_bytes", "jssa_kp_page_bytes", "jssa_store", "jssa_select",
+EXPORTED = ("jssa_status_string", "jssa_workspace_bytes", "jssa_decode_path", "jssa_kp_page_bytes", "jssa_store",
+            "jssa_select",
             "jssa_select_stages",
             "jssa_attend", "jssa_decode", "jssa_full_decode", "jssa_gather_attend", "jssa_calib_workspace_bytes",
             "jssa_calib_moments", "jssa_basis")
@@ -65,6 +66,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "jssa_status_string": (ctypes.c_char_p, [I32]),
         "jssa_workspace_bytes": (I32, [S, ctypes.POINTER(SZ)]),
+        "jssa_decode_path": (I32, [S, ctypes.POINTER(I32)]),
         "jssa_kp_page_bytes": (I32, [S, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
         "jssa_store": (I32, [S, P, P, I32, P, P, P, P]),
         "jssa_select": (I32, [S, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -115,6 +117,13 @@ def workspace_bytes(shape: Shape) -> int:
     n = ctypes.c_size_t()
     _check("jssa_workspace_bytes", _lib.jssa_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)))
     return n.value
+
+
+def decode_single_launch(shape: Shape) -> bool:
+    """Whether jssa_decode runs this shape as one launch per layer."""
+    v = ctypes.c_int32()
+    _check("jssa_decode_path", _lib.jssa_decode_path(ctypes.byref(shape), ctypes.byref(v)))
+    return bool(v.value)
 
 
 def kp_page_bytes(shape: Shape) -> Tuple[int, int]:

@@ -302,6 +302,17 @@ int32_t jssa_workspace_bytes(const jssa_shape* shape, size_t* bytes) {
   return JSSA_OK;
 }
 
+int32_t jssa_decode_path(const jssa_shape* shape, int32_t* single) {
+  if (!single) return JSSA_ERR_NULL;
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  const bool fits = fused_applies(p.mla, p.d, p.G, p.r, p.maxN, p.B);
+  if (shape->select_mode == JSSA_SELECT_FUSED && !fits) return JSSA_ERR_UNSUPPORTED;
+  *single = (shape->select_mode == JSSA_SELECT_FUSED || (shape->select_mode == JSSA_SELECT_AUTO && fits)) ? 1 : 0;
+  return JSSA_OK;
+}
+
 int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page, int64_t* scale_elems_per_page) {
   if (!kp_bytes_per_page || !scale_elems_per_page) return JSSA_ERR_NULL;
   Plan p;
@@ -367,10 +378,10 @@ int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
   if (!p.mla && !v_cache) return JSSA_ERR_NULL;
   if (k_new && !slot_new) return JSSA_ERR_NULL;
   if (workspace_bytes < p.total) return JSSA_ERR_WORKSPACE;
-  const int mode = shape->select_mode;
-  const bool fits = fused_applies(p.mla, p.d, p.G, p.r, p.maxN, p.B);
-  if (mode == JSSA_SELECT_FUSED && !fits) return JSSA_ERR_UNSUPPORTED;
-  if (mode == JSSA_SELECT_FUSED || (mode == JSSA_SELECT_AUTO && fits)) {
+  int32_t single = 0;
+  st = jssa_decode_path(shape, &single);
+  if (st != JSSA_OK) return st;
+  if (single) {
     FusedArgs f{};
     f.q = q;
     f.k_new = k_new;

@@ -55,6 +55,37 @@ def test_shape_validation(kw, status):
     assert st == status
 
 
+@pytest.mark.parametrize("kw,mode,single", [
+    # the tiny workload's shape: capacity 4096, G = 4, d = 128, r = 32
+    (dict(batch=1, num_q_heads=8, num_kv_heads=2, max_pages_per_seq=256, budget=256), L.SELECT_AUTO, 1),
+    (dict(batch=1, num_q_heads=8, num_kv_heads=2, max_pages_per_seq=256, budget=256), L.SELECT_FUSED, 1),
+    (dict(batch=1, num_q_heads=8, num_kv_heads=2, max_pages_per_seq=256, budget=256), L.SELECT_SPLIT, 0),
+    (dict(batch=1, num_q_heads=8, num_kv_heads=2, max_pages_per_seq=256, budget=256), L.SELECT_EXACT_STREAM, 0),
+    (dict(max_pages_per_seq=768), L.SELECT_AUTO, 1),                      # capacity 12288: the limit
+    (dict(max_pages_per_seq=769), L.SELECT_AUTO, 0),                      # one page more
+    (dict(max_pages_per_seq=769), L.SELECT_FUSED, -3),
+    (dict(max_pages_per_seq=192, page_size=64), L.SELECT_AUTO, 1),        # 12288 tokens in pages of 64
+    (dict(max_pages_per_seq=256, num_q_heads=64), L.SELECT_AUTO, 0),      # G = 8: G * d = 1024
+    (dict(max_pages_per_seq=256, head_dim=256, num_q_heads=16), L.SELECT_AUTO, 1),   # d = 256, G = 2
+    (dict(max_pages_per_seq=256, head_dim=256), L.SELECT_AUTO, 0),        # d = 256, G = 4
+    (dict(max_pages_per_seq=256, rank=64), L.SELECT_AUTO, 1),
+    (dict(max_pages_per_seq=256, rank=80), L.SELECT_AUTO, 0),             # r > 64
+    (dict(max_pages_per_seq=256, rank=80), L.SELECT_FUSED, -3),
+    (dict(max_pages_per_seq=256, budget=4096), L.SELECT_AUTO, 1),
+    (dict(), L.SELECT_AUTO, 0),                                           # the 128K layer: split path
+    (dict(kind=1, num_kv_heads=1, num_q_heads=128, head_dim=576, rank=64, page_size=64, max_pages_per_seq=64),
+     L.SELECT_AUTO, 0),                                                   # MLA: split path
+])
+def test_decode_path(kw, mode, single):
+    """Which path jssa_decode takes (the single launch covers GQA with capacity <= 12288, r <= 64, G * d <= 512)."""
+    v = ctypes.c_int32(-7)
+    st = L.raw_library().jssa_decode_path(ctypes.byref(_shape(select_mode=mode, **kw)), ctypes.byref(v))
+    if single < 0:
+        assert st == single
+    else:
+        assert st == 0 and v.value == single
+
+
 def test_workspace_and_page_sizes():
     s = _shape()
     ws = L.workspace_bytes(s)

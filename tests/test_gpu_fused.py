@@ -179,6 +179,7 @@ def test_fused_empty_sequence_and_auto():
     split = _decode(w, case, m32, rows_k, "fp32", L.SELECT_SPLIT, seq_lens=sl)
     _compare(split, fused)
     _check_oracle(w, case, m32, rows_k, rows_v, "fp32", fused, seq_lens=sl)
+    assert L.decode_single_launch(L.shape_for(w))                 # AUTO takes the single launch here
     auto = _decode(w, case, m32, rows_k, "fp32", L.SELECT_AUTO, seq_lens=sl)
     for a, f in zip(auto, fused):
         assert (a is None and f is None) or np.array_equal(a, f, equal_nan=True)
