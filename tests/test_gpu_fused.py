@@ -204,3 +204,20 @@ def test_fused_refuses_uncovered_shapes():
                           torch.zeros((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=DEV),
                           w.sm_scale, t(w.batch, w.num_q_heads, w.head_dim), ws)
         assert err.value.status == -3                        # JSSA_ERR_UNSUPPORTED
+
+
+def test_select_treats_split_and_fused_as_auto():
+    """jssa_select has no single-launch variant: SPLIT and FUSED select exactly as AUTO does."""
+    w, case, m32, rows_k, rows_v = _case("cap_12k")
+    M = torch.from_numpy(m32).to(DEV)
+    kp, ks = _stored_cache(w, L.shape_for(w), case, M)
+    got = {}
+    for mode in (L.SELECT_AUTO, L.SELECT_SPLIT, L.SELECT_FUSED):
+        shape = L.shape_for(w, select_mode=mode)
+        idx = torch.full((w.batch, w.num_kv_heads, w.budget), 7, dtype=torch.int32, device=DEV)
+        L.jssa_select(shape, case.layers[0].q.to(DEV), M, kp, ks, case.block_table.to(DEV), case.seq_lens.to(DEV),
+                      idx, L.alloc_workspace(shape))
+        torch.cuda.synchronize()
+        got[mode] = idx.cpu().numpy()
+    assert np.array_equal(got[L.SELECT_AUTO], got[L.SELECT_SPLIT])
+    assert np.array_equal(got[L.SELECT_AUTO], got[L.SELECT_FUSED])
