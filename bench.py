@@ -32,6 +32,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import re
 import json
 import os
 import sys
@@ -53,11 +54,21 @@ def counters_path(workload):
     return os.path.join(ROOT, "profiles", f"counters_select_stream_{workload}.json")
 
 
+def _code_lines(text: str):
+    """The source's code without comments and blank lines (a comment edit leaves the hash alone)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    for line in text.splitlines():
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            yield line
+
+
 def _src_hash(*names):
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "long_context_decode_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "long_context_decode_amd", "csrc", n)) as f:
+            for line in _code_lines(f.read()):
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -13,9 +13,10 @@
 //     for a group of KV heads; a block's four wavefronts form one chunk):
 //     every lane owns one (KV head, slot) and reads that token's 16-byte
 //     pieces (FP8 codes, or BF16 keys: twice the pieces, half the pages) for
-//     all pages at once (a wavefront reads one contiguous run per piece),
-//     scores them, and the keys >= tau are compacted in position order
-//     straight from the ballot masks into the chunk's region of the
+//     all pages at once with streaming (non-temporal) loads, since each
+//     byte is read once per step (a wavefront reads one contiguous run per
+//     piece), scores them, and the keys >= tau are compacted in position
+//     order straight from the ballot masks into the chunk's region of the
 //     candidate buffer; the chunk's count is recorded.
 //  3. finish    (one 1024-thread block per (sequence, KV head)): gathers the
 //     candidates into LDS in chunk order (so they are in position order),
