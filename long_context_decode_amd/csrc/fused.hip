@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   constexpr int NF = D / 32;     // float4 groups of a row of M per thread
   constexpr int TPT = 4 / R;     // tokens per thread with loads in flight together (<= 8 pieces)
   constexpr int GRP = 4;         // rows whose loads are in flight together
+  constexpr bool VE = NV == 1;   // d = 128: the first group's V rows go out with its K rows
   const int h = blockIdx.x, b = blockIdx.y, tid = (int)threadIdx.x, lane = lane_id(), w = tid >> 6;
   const int row = lane >> 4, c16 = lane & 15;
   const bool bf = a.sfmt == 3;
@@ -240,6 +241,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     float xs[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) xs[g] = -INFINITY;
+    uint4 v0r[GRP][NV];                        // the first group's V rows (d = 128: requested with its K rows)
 #pragma unroll
     for (int u0 = 0; u0 < 16; u0 += GRP) {   // compile-time lane indices for the row broadcasts
       if (u0 >= iters) break;                  // uniform
@@ -250,6 +252,15 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
         const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
 #pragma unroll
         for (int v = 0; v < NV; ++v) kr[u][v] = *reinterpret_cast<const uint4*>(kbase + ro + v * 128);
+      }
+      if (VE && u0 == 0) {
+#pragma unroll
+        for (int u = 0; u < GRP; ++u) {
+          const int rr = row_bcast(ri, u);
+          const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
+#pragma unroll
+          for (int v = 0; v < NV; ++v) v0r[u][v] = *reinterpret_cast<const uint4*>(vbase + ro + v * 128);
+        }
       }
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {
@@ -295,7 +306,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
         const int rr = row_bcast(ri, u0 + u);
         const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) vr[u][v] = *reinterpret_cast<const uint4*>(vbase + ro + v * 128);
+        for (int v = 0; v < NV; ++v)
+          vr[u][v] = (VE && u0 == 0) ? v0r[u][v] : *reinterpret_cast<const uint4*>(vbase + ro + v * 128);
       }
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {
