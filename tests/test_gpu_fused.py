@@ -221,3 +221,35 @@ def test_select_treats_split_and_fused_as_auto():
         got[mode] = idx.cpu().numpy()
     assert np.array_equal(got[L.SELECT_AUTO], got[L.SELECT_SPLIT])
     assert np.array_equal(got[L.SELECT_AUTO], got[L.SELECT_FUSED])
+
+
+def _sweep_cases():
+    """A seeded sample of small shapes the single launch covers: d, G, page, r, B (odd ones too) and N."""
+    rng = np.random.default_rng(7)
+    out = []
+    for i in range(10):
+        d = int(rng.choice([128, 256]))
+        g = int(rng.choice([1, 2, 4] if d == 128 else [1, 2]))
+        hkv = int(rng.choice([1, 2, 3]))
+        page = int(rng.choice([16, 32, 64]))
+        r = int(rng.choice([16, 32, 48, 64]))
+        budget = int(rng.choice([1, 17, 256, 1000]))
+        seq = int(rng.integers(200, 6000))
+        out.append(_w(name=f"s{i}", batch=2, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, page_size=page,
+                      rank=r, budget=budget, seq_len=seq, calib_seqs=1, calib_len=512))
+    return out
+
+
+@pytest.mark.parametrize("w", _sweep_cases(), ids=lambda w: w.name)
+def test_fused_equals_split_sweep(w):
+    q, k = make_gqa_calibration(w, 0)
+    m32 = ocal.calibrate(ocal.bf16_to_f64(bf16_bits(q)), ocal.bf16_to_f64(bf16_bits(k)), w.group,
+                         w.rank).astype(np.float32)
+    case = make_gqa_case(w, ragged=True)
+    lay = case.layers[0]
+    bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
+    rows_k = [ogqa.logical_rows(bf16_bits(lay.k_cache), bt[b], int(sl[b]), w.page_size) for b in range(w.batch)]
+    assert L.decode_single_launch(L.shape_for(w))
+    split = _decode(w, case, m32, rows_k, "fp32", L.SELECT_SPLIT)
+    fused = _decode(w, case, m32, rows_k, "fp32", L.SELECT_FUSED)
+    _compare(split, fused)
