@@ -68,6 +68,7 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k
   if (l == js) {
     bcast[0] = (uint32_t)(ls * 32 + js);
     bcast[1] = k - excl;
+    bcast[2] = cj;                       // keys in the digit's bin
   }
 }
 
@@ -79,7 +80,10 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k
 //
 // With stop_shift > 0 the digits below bit stop_shift are not resolved: *kth
 // is then the lower edge (low bits zero) of the bin holding the k-th key, a
-// bound <= the k-th key, and *need is not meaningful.
+// bound <= the k-th key, and *need is not meaningful.  With stop_shift == 0,
+// once the k-th key's bin holds exactly the keys still needed (all of them
+// belong to the top k), the passes end: *kth is then one below the bin's
+// lower edge and *need is 0, which selects the same set (key > *kth).
 template <int NT>
 __device__ void block_radix_select(const uint32_t* keys, int n, uint32_t k, uint32_t* hist2, uint32_t* tmp,
                                    uint32_t* kth, uint32_t* need, int stop_shift = 0) {
@@ -114,6 +118,12 @@ __device__ void block_radix_select(const uint32_t* keys, int n, uint32_t k, uint
     hi_mask = ~((1u << shift) - 1u);
     prefix &= hi_mask;
     if (shift <= stop_shift) break;
+    if (stop_shift == 0 && tmp[50] == k && prefix > 0u) {
+      *kth = prefix - 1u;
+      *need = 0u;
+      __syncthreads();                 // tmp is reused by the caller
+      return;
+    }
     hb = shift - 1;
   }
   *kth = prefix;
