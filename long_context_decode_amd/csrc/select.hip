@@ -138,10 +138,12 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
   int sp = 0, n_pages = 0;
   if (sampled) {
     n_pages = (N + a.P - 1) / a.P;
-    // about 64 samples per expected selection, at least 2048, and no more
-    // than 256 KB of scoring cache (one CU reads the whole sample)
+    // about 32 samples per expected selection (so that ks, the sampled keys
+    // above tau, is about 64: the candidate count then varies by about 1/8),
+    // at least 2048, and no more than 256 KB of scoring cache (one CU reads
+    // the whole sample)
     constexpr int kByteCap = (256 * 1024) / (RP * 16);
-    int64_t want = (int64_t)64 * N / a.B;
+    int64_t want = (int64_t)32 * N / a.B;
     if (want > kByteCap) want = kByteCap;
     if (want < 2048) want = 2048;
     if (want > kSampleMax) want = kSampleMax;
