@@ -140,12 +140,12 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     n_pages = (N + a.P - 1) / a.P;
     // about 32 samples per expected selection (so that ks, the sampled keys
     // above tau, is about 64: the candidate count then varies by about 1/8),
-    // at least 2048, and no more than 256 KB of scoring cache (one CU reads
-    // the whole sample)
+    // at least 1024 (where that floor applies, ks = 2B 1024 / N >= 64), and
+    // no more than 256 KB of scoring cache (one CU reads the whole sample)
     constexpr int kByteCap = (256 * 1024) / (RP * 16);
     int64_t want = (int64_t)32 * N / a.B;
     if (want > kByteCap) want = kByteCap;
-    if (want < 2048) want = 2048;
+    if (want < 1024) want = 1024;
     if (want > kSampleMax) want = kSampleMax;
     sp = (int)((want + a.P - 1) / a.P);
     if (sp > kSampleMax / a.P) sp = kSampleMax / a.P;
