@@ -253,3 +253,48 @@ def test_fused_equals_split_sweep(w):
     split = _decode(w, case, m32, rows_k, "fp32", L.SELECT_SPLIT)
     fused = _decode(w, case, m32, rows_k, "fp32", L.SELECT_FUSED)
     _compare(split, fused)
+
+
+def test_fused_graph_replay_matches_eager():
+    """The single launch captured in a HIP graph replays bit-identically to the eager call, with eager work
+    between the replays (the new token is stored each time: the same bytes)."""
+    w, case, m32, rows_k, rows_v = _case("tiny_b3")
+    shape = L.shape_for(w, select_mode=L.SELECT_FUSED)
+    M = torch.from_numpy(m32).to(DEV)
+    kp, ks = _stored_cache(w, shape, case, M)
+    bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
+    new_slot = torch.tensor([bt[b, (sl[b] - 1) // w.page_size] * w.page_size + (sl[b] - 1) % w.page_size
+                             for b in range(w.batch)], dtype=torch.int32, device=DEV)
+    k_new = torch.from_numpy(np.stack([rows_k[b][int(sl[b]) - 1] for b in range(w.batch)]).view(np.int16)) \
+        .view(torch.bfloat16).to(DEV)
+    lay = case.layers[0]
+    q, kc, vc = lay.q.to(DEV), lay.k_cache.to(DEV), lay.v_cache.to(DEV)
+    btd, sld = case.block_table.to(DEV), case.seq_lens.to(DEV)
+    ws = L.alloc_workspace(shape)
+    idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+
+    def step():
+        L.jssa_decode(shape, q, k_new, new_slot, M, kp, ks, kc, vc, btd, sld, idx, w.sm_scale, out, ws, lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (idx.clone(), out.clone(), lse.clone(), kp.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        idx.fill_(-7)
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0]), rep
+        assert torch.equal(out.view(torch.int16), ref[1].view(torch.int16)), rep
+        assert torch.equal(lse, ref[2]), rep
+        assert torch.equal(kp, ref[3]), rep
+        step()                                    # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0])
