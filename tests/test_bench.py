@@ -65,3 +65,18 @@ def test_trace_summary(tmp_path):
     lines = txt.splitlines()
     assert "select_stream" in lines[6] and "5.00" in lines[6]
     assert "other kernels" in lines[-1] and lines[-1].split("|")[2].strip() == "3"
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    """The counters are keyed to the stream's code: a comment or blank-line edit keeps the key, a code edit
+    changes it."""
+    csrc = tmp_path / "long_context_decode_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    f = csrc / "k.hip"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    f.write_text("int a = 1;  // one\n/* block\n comment */ int b = 2;\n")
+    h0 = bench._src_hash("k.hip")
+    f.write_text("// new header\n\nint a = 1;  // changed words\n/* other */ int b = 2;\n\n")
+    assert bench._src_hash("k.hip") == h0
+    f.write_text("int a = 1;\nint b = 3;\n")
+    assert bench._src_hash("k.hip") != h0
