@@ -66,18 +66,19 @@ def _logical(cache, bt_row, n, P):
 
 
 def _pair_codes(kp, ks, bt_row, n, P, h):
-    """GPU codes [n, S] and scales [n] of KV head h of one sequence from the piece-major scoring cache."""
+    """GPU codes [n, S] (BF16 keys: [n, 2S] bytes) and scales [n] (None without a scale array) of KV head h
+    of one sequence from the piece-major scoring cache."""
     npg = -(-n // P)
     pages = bt_row.long()[:npg]
-    c = kp[pages, h]                                  # [npg, S/16, P, 16]
+    c = kp[pages, h]                                  # [npg, pieces, P, 16]
     c = c.permute(0, 2, 1, 3).reshape(npg * P, -1)[:n]
-    s = ks[pages, h].reshape(-1)[:n]
-    return c.cpu().numpy(), s.cpu().numpy()
+    s = None if ks is None else ks[pages, h].reshape(-1)[:n].cpu().numpy()
+    return c.cpu().numpy(), s
 
 
-def _run_gqa(name, layer, window_layer):
+def _run_gqa(name, layer, window_layer, fmt="fp32", full=True):
     w = WORKLOADS[name]
-    shape = L.shape_for(w)
+    shape = L.shape_for(w, scale_format=L.SCALE_FORMATS[fmt])
     case = make_gqa_case(w, device=DEV, layers=[layer])
     lay = case.layers[layer]
     bt, sl = case.block_table, case.seq_lens
@@ -85,7 +86,8 @@ def _run_gqa(name, layer, window_layer):
     lse_f = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
     ws = L.alloc_workspace(shape)
     window = w.window if window_layer else 0
-    L.jssa_full_decode(shape, lay.q, lay.k_cache, lay.v_cache, bt, sl, window, w.sm_scale, out_f, ws, lse_f)
+    if full:
+        L.jssa_full_decode(shape, lay.q, lay.k_cache, lay.v_cache, bt, sl, window, w.sm_scale, out_f, ws, lse_f)
     res = dict(w=w, case=case, lay=lay, out_f=out_f.float().cpu().numpy(), lse_f=lse_f.cpu().numpy())
     if window_layer:
         return res
@@ -139,6 +141,34 @@ def test_fullsize_gqa_decode_step(name, layer):
             o, l = ogqa.attend(q[b, j], rk, rv, w.sm_scale)
             check_attention(r["out_f"][b, j], o)
             assert abs(r["lse_f"][b, j] - l) <= 1e-3
+    del r
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["e8m0", "none", "bf16"])
+def test_fullsize_scale_formats(fmt):
+    """The 128K layer at its benchmark shape with the other scoring-cache formats: bulk store, one decode step
+    (new token stored inside it); on two (sequence, KV head) pairs the selection against the oracle's top-B on
+    the GPU's own codes and the attention against fp64 attention over the GPU's set."""
+    r = _run_gqa("llama8b_128k", 0, window_layer=False, fmt=fmt, full=False)
+    w, case, lay = r["w"], r["case"], r["lay"]
+    q = bf16_bits(lay.q)
+    G, P = w.group, w.page_size
+    for b, h in _pairs(w)[:2]:
+        n = int(case.seq_lens[b])
+        rk = bf16_bits(_logical(lay.k_cache, case.block_table[b], n, P)[:, h])
+        rv = bf16_bits(_logical(lay.v_cache, case.block_table[b], n, P)[:, h])
+        codes, scale = _pair_codes(r["kp"], r["ks"], case.block_table[b], n, P, h)
+        qhat = ogqa.project_query(q[b], r["m32"], G)[h]
+        sc = ogqa.scores(qhat, codes, scale, fmt)
+        oidx, tau = ogqa.select_topb(sc, w.budget)
+        check_selection(r["idx"][b, h], oidx, sc, tau)
+        sel = r["idx"][b, h][r["idx"][b, h] >= 0]
+        for g in range(G):
+            j = h * G + g
+            o, l = ogqa.attend(q[b, j], rk[sel], rv[sel], w.sm_scale)
+            check_attention(r["out"][b, j], o)
+            assert abs(r["lse"][b, j] - l) <= 1e-3
     del r
     torch.cuda.empty_cache()
 
