@@ -234,3 +234,42 @@ def test_fullsize_mla_decode_step():
         check_attention(gotf[b], o)
         assert np.all(np.abs(glsef[b] - l) <= 1e-3)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["e8m0", "bf16"])
+def test_fullsize_mla_scale_formats(fmt):
+    """The 128K MLA layer at its benchmark shape with the one-byte scale and with BF16 keys: bulk store, one
+    decode step; on two sequences the selection against the oracle's top-B on the GPU's own codes and the
+    attention against fp64 attention over the GPU's set."""
+    name = "mla_128k"
+    w = WORKLOADS[name]
+    shape = L.shape_for(w, scale_format=L.SCALE_FORMATS[fmt])
+    case = make_mla_case(w, device=DEV)
+    bt, sl, P = case.block_table, case.seq_lens, w.page_size
+    m32 = _mla_basis(name)
+    M = torch.from_numpy(m32).to(DEV)
+    kp, ks = L.alloc_scoring_cache(shape, case.latent.shape[0], DEV)
+    flat = case.latent.view(-1, w.head_dim)
+    _bulk_store(w, shape, flat, bt, sl, M, kp, ks)
+    last = sl.long() - 1
+    slot_new = (bt.long()[torch.arange(w.batch, device=DEV), last // P] * P + last % P).to(torch.int32)
+    k_new = flat[slot_new.long()].contiguous()
+    idx = torch.empty((w.batch, 1, w.budget), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    L.jssa_decode(shape, case.q, k_new, slot_new, M, kp, ks, case.latent, None, bt, sl, idx, w.sm_scale, out,
+                  L.alloc_workspace(shape), lse)
+    torch.cuda.synchronize()
+    gidx, got, glse = idx.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy()
+    q = bf16_bits(case.q)
+    for b in (0, w.batch - 1):
+        n = int(sl[b])
+        rows = bf16_bits(_logical(case.latent, bt[b], n, P))
+        codes, scale = _pair_codes(kp, ks, bt[b], n, P, 0)
+        sc = ogqa.scores(omla.project_query(q[b], m32), codes, scale, fmt)
+        oidx, tau = ogqa.select_topb(sc, w.budget)
+        check_selection(gidx[b, 0], oidx, sc, tau)
+        o, l = omla.attend(q[b], rows[gidx[b, 0][gidx[b, 0] >= 0]], w.sm_scale)
+        check_attention(got[b], o)
+        assert np.all(np.abs(glse[b] - l) <= 1e-3)
+    torch.cuda.empty_cache()
