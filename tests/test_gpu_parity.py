@@ -44,6 +44,8 @@ GQA_CASES = {
     "short_ctx": (_w("tiny", name="short", model="test", batch=2, seq_len=300, budget=512), True),
     "page32_g8": (_w("tiny", name="p32", model="test", batch=2, num_q_heads=16, num_kv_heads=2, page_size=32,
                      seq_len=9000, budget=1000), True),
+    # the largest budget (4096): the sampled threshold aims at 6144 candidates, under 2B
+    "max_budget": (_w("tiny", name="maxb", model="test", batch=2, seq_len=40000, budget=4096), True),
 }
 
 
@@ -222,7 +224,7 @@ def test_select_needles_and_determinism():
 
 # ----------------------------------------------------------------------------- attend
 
-@pytest.mark.parametrize("name", ["tiny", "mid_sampled", "d256_r48", "short_ctx", "page32_g8"])
+@pytest.mark.parametrize("name", ["tiny", "mid_sampled", "d256_r48", "short_ctx", "page32_g8", "max_budget"])
 def test_attend_parity(name):
     w, case, m32, rows_k, rows_v, stored = _gqa(name)
     q = bf16_bits(case.layers[0].q)
