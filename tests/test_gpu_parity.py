@@ -322,6 +322,7 @@ def test_decode_step_stores_new_token_then_selects_and_attends():
 MLA_CASES = {
     "tiny_mla": _w("tiny_mla"),
     "mla_sampled": _w("tiny_mla", name="mla_mid", model="test", batch=2, seq_len=40000, budget=1024),
+    "mla_max_budget": _w("tiny_mla", name="mla_maxb", model="test", batch=2, seq_len=40000, budget=4096),
 }
 
 
