@@ -46,6 +46,9 @@ GQA_CASES = {
                      seq_len=9000, budget=1000), True),
     # the largest budget (4096): the sampled threshold aims at 6144 candidates, under 2B
     "max_budget": (_w("tiny", name="maxb", model="test", batch=2, seq_len=40000, budget=4096), True),
+    # 12325, 12288 and 12251 tokens: sampled threshold above the 12288-token candidate capacity, every
+    # token a candidate at and below it
+    "cap_edge": (_w("tiny", name="capedge", model="test", batch=3, seq_len=12325, budget=1024), True),
 }
 
 
@@ -224,7 +227,8 @@ def test_select_needles_and_determinism():
 
 # ----------------------------------------------------------------------------- attend
 
-@pytest.mark.parametrize("name", ["tiny", "mid_sampled", "d256_r48", "short_ctx", "page32_g8", "max_budget"])
+@pytest.mark.parametrize("name", ["tiny", "mid_sampled", "d256_r48", "short_ctx", "page32_g8", "max_budget",
+                                  "cap_edge"])
 def test_attend_parity(name):
     w, case, m32, rows_k, rows_v, stored = _gqa(name)
     q = bf16_bits(case.layers[0].q)
