@@ -259,7 +259,9 @@ def test_attend_parity(name):
 
 
 @pytest.mark.parametrize("name,window", [("tiny", 0), ("tiny", 1024), ("d256_r48", 0), ("d256_r48", 1000),
-                                         ("short_ctx", 100), ("page32_g8", 0)])
+                                         ("short_ctx", 100), ("page32_g8", 0),
+                                         ("short_ctx", 1),       # a single position
+                                         ("short_ctx", 5000)])   # wider than every sequence: all positions
 def test_full_decode_parity(name, window):
     w, case, m32, rows_k, rows_v, _ = _gqa(name)
     q = bf16_bits(case.layers[0].q)
@@ -519,7 +521,7 @@ def test_mla_decode_step():
         check_attention(got[b], o)
 
 
-@pytest.mark.parametrize("name,window", [("tiny_mla", 0), ("mla_sampled", 0), ("mla_sampled", 1000)])
+@pytest.mark.parametrize("name,window", [("tiny_mla", 0), ("mla_sampled", 0), ("mla_sampled", 1000), ("tiny_mla", 1)])
 def test_mla_full_decode_parity(name, window):
     """Dense MLA baseline (all positions, or the last `window`) on the matrix cores."""
     w, case, m32, rows, stored = _mla(name)
