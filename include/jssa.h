@@ -151,6 +151,7 @@ int32_t jssa_kp_page_bytes(const jssa_shape* shape, int64_t* kp_bytes_per_page,
  *   JSSA_KEYS_BF16: y rounded to bf16 (nearest, ties to even), no scale.
  * k_new : GQA bf16 [T, Hkv, d]; MLA bf16 [T, 576]
  * slot  : int32 [T], physical page * page_size + slot in page; < 0 skips the row
+ * T = 0 returns JSSA_OK at once (no pointer is read, nothing is launched); T < 0 is JSSA_ERR_SHAPE.
  * M     : GQA fp32 [Hkv, r, d]; MLA fp32 [r, 512]
  * kp, kp_scale : the scoring cache (layout above), written at the slots only
  *                (kp_scale may be NULL with JSSA_SCALE_NONE or JSSA_KEYS_BF16). */

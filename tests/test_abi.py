@@ -104,6 +104,13 @@ def test_workspace_and_page_sizes():
     assert L.raw_library().jssa_workspace_bytes(ctypes.byref(_shape(scale_format=4)), ctypes.byref(n)) == -3
 
 
+def test_store_of_no_tokens_is_a_no_op_before_any_check():
+    """T = 0 returns success before the pointers are looked at: nothing is launched (no device here)."""
+    null = ctypes.c_void_p(0)
+    assert L.raw_library().jssa_store(ctypes.byref(_shape()), null, null, 0, null, null, null, null) == 0
+    assert L.raw_library().jssa_store(ctypes.byref(_shape()), null, null, -1, null, null, null, null) != 0
+
+
 def test_entry_points_reject_before_launch():
     """Errors come back from host validation; nothing touches the device (there is none here)."""
     lib = L.raw_library()

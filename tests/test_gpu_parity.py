@@ -182,6 +182,20 @@ def test_store_skips_negative_slots_and_zero_rows():
     assert np.all(c[untouched] == 0xAB) and np.all(s[untouched] == 7.0)
 
 
+def test_store_of_no_tokens_changes_nothing():
+    """T = 0: the call succeeds and launches nothing; the scoring cache and its scales keep their bytes."""
+    w = _w("tiny")
+    shape = L.shape_for(w)
+    kp, ks = L.alloc_scoring_cache(shape, 4, DEV)
+    kp.fill_(0xAB)
+    ks.fill_(7.0)
+    k_new = torch.zeros((0, w.num_kv_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    slot = torch.zeros((0,), dtype=torch.int32, device=DEV)
+    L.jssa_store(shape, k_new, slot, torch.from_numpy(_basis(w)).to(DEV), kp, ks)
+    torch.cuda.synchronize()
+    assert bool((kp == 0xAB).all()) and bool((ks == 7.0).all())
+
+
 # ----------------------------------------------------------------------------- select
 
 def _run_select(name, mode=0):
