@@ -134,6 +134,18 @@ int32_t jssa_workspace_bytes(const jssa_shape* shape, size_t* bytes);
  * jssa_decode would. */
 int32_t jssa_decode_path(const jssa_shape* shape, int32_t* single);
 
+/* Split-K plan of one attention call of this shape (the summary page's §3.3
+ * Gather-Free Indexed Attention splits a head's positions over several
+ * workgroups whose partial results are merged by log-sum-exp): *splits is the
+ * number of position ranges jssa_attend (sparse != 0) or jssa_full_decode
+ * with this window (sparse == 0; window 0 = every position) uses per
+ * (sequence, KV head), and *capacity the number the workspace of
+ * jssa_workspace_bytes holds; *splits <= *capacity for every window.
+ * Returns JSSA_ERR_NULL for a NULL output, JSSA_ERR_SHAPE for window < 0 and
+ * the shape's own validation status otherwise.  Launches nothing. */
+int32_t jssa_attend_splits(const jssa_shape* shape, int32_t sparse, int32_t window, int32_t* splits,
+                           int32_t* capacity);
+
 /* Bytes of the projected scoring cache per page (kp) and scale elements per
  * page (kp_scale: fp32 for JSSA_SCALE_FP32, bytes for JSSA_SCALE_E8M0, 0 for
  * JSSA_SCALE_NONE and JSSA_KEYS_BF16), so callers can size both buffers. */

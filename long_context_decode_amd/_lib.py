@@ -26,7 +26,8 @@ SCALE_FORMATS = {"fp32": SCALE_FP32, "e8m0": SCALE_E8M0, "none": SCALE_NONE, "bf
 STAGE_PROLOGUE, STAGE_STREAM, STAGE_FINISH, STAGE_ALL = 1, 2, 4, 7
 MLA_LATENT, MLA_ROPE = 512, 64
 
-EXPORTED = ("jssa_status_string", "jssa_workspace_bytes", "jssa_decode_path", "jssa_kp_page_bytes", "jssa_store",
+EXPORTED = ("jssa_status_string", "jssa_workspace_bytes", "jssa_decode_path", "jssa_attend_splits",
+            "jssa_kp_page_bytes", "jssa_store",
             "jssa_select",
             "jssa_select_stages",
             "jssa_attend", "jssa_decode", "jssa_full_decode", "jssa_gather_attend", "jssa_calib_workspace_bytes",
@@ -67,6 +68,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "jssa_status_string": (ctypes.c_char_p, [I32]),
         "jssa_workspace_bytes": (I32, [S, ctypes.POINTER(SZ)]),
         "jssa_decode_path": (I32, [S, ctypes.POINTER(I32)]),
+        "jssa_attend_splits": (I32, [S, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "jssa_kp_page_bytes": (I32, [S, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
         "jssa_store": (I32, [S, P, P, I32, P, P, P, P]),
         "jssa_select": (I32, [S, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -124,6 +126,14 @@ def decode_single_launch(shape: Shape) -> bool:
     v = ctypes.c_int32()
     _check("jssa_decode_path", _lib.jssa_decode_path(ctypes.byref(shape), ctypes.byref(v)))
     return bool(v.value)
+
+
+def attend_splits(shape: Shape, sparse: bool, window: int = 0) -> Tuple[int, int]:
+    """(splits an attention call of this shape uses, splits the workspace holds)."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check("jssa_attend_splits", _lib.jssa_attend_splits(ctypes.byref(shape), int(bool(sparse)), int(window),
+                                                         ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 def kp_page_bytes(shape: Shape) -> Tuple[int, int]:

@@ -26,6 +26,7 @@ struct Plan {
   int ml_splits, ml_len;     // MLA sparse attention split plan
   int md_splits, md_len;     // MLA dense (window 0) split plan
   int stage_pages;            // gather-then-attend staging cache: pages per sequence
+  int split_cap;              // splits the workspace's partials hold per (sequence, query head)
   size_t off_qhat, off_tau, off_chunk, off_cand, off_part_o, off_part_ml;
   size_t off_stage_k, off_stage_v, off_stage_table, off_stage_lens, total;
 };
@@ -59,6 +60,17 @@ void mla_dense_plan(int64_t n, int batch, int Hq, int* splits, int* len) {
   sp = std::max<int64_t>(1, std::min<int64_t>({sp, cdiv(n, 128), 256}));
   *len = (int)(cdiv(cdiv(n, sp), 64) * 64);
   *splits = (int)cdiv(n, *len);
+}
+
+// Most splits a plan of this shape can take, whatever the row count: the
+// GQA plan takes at most min(cdiv(512, pairs), 64) splits, the MLA dense plan
+// at most min(cdiv(512, batch * head blocks of 64), 256) and the MLA sparse
+// plan at most min(cdiv(512, batch * head blocks of 32), 64).
+int split_capacity(const Plan& p) {
+  if (!p.mla) return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(512, (int64_t)p.batch * p.Hkv), 64));
+  const int64_t dense = std::min<int64_t>(cdiv(512, (int64_t)p.batch * cdiv(p.Hq, 64)), 256);
+  const int64_t sparse = std::min<int64_t>(cdiv(512, (int64_t)p.batch * std::max(1, p.Hq / 32)), 64);
+  return (int)std::max<int64_t>(1, std::max(dense, sparse));
 }
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -139,9 +151,15 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   p->off_tau = off;     off = align_up(off + bh * sizeof(uint32_t));
   p->off_chunk = off;   off = align_up(off + bh * p->max_chunks * sizeof(int32_t));
   p->off_cand = off;    off = align_up(off + cand * 2 * sizeof(uint32_t));
-  const int gqa_splits = std::max({p->sp_splits, p->dn_splits, st_splits});
-  // split-K partials: one per block for MLA, one per wavefront (4 per split) for GQA
-  const size_t parts = p->mla ? (size_t)std::max({p->ml_splits, p->md_splits, st_splits}) : (size_t)gqa_splits * 4;
+  // split-K partials: one per block for MLA, one per wavefront (4 per split)
+  // for GQA.  Sized for the most splits any plan of this shape can take: a
+  // window shorter than the capacity rounds its split length to fewer rows
+  // than the full plan does and may therefore take more splits than it.
+  p->split_cap = split_capacity(*p);
+  const size_t parts = p->mla ? (size_t)p->split_cap : (size_t)p->split_cap * 4;
+  const int most = p->mla ? std::max({p->ml_splits, p->md_splits, st_splits})
+                          : std::max({p->sp_splits, p->dn_splits, st_splits});
+  if (most > p->split_cap) return JSSA_ERR_UNSUPPORTED;   // cannot happen: split_capacity bounds every plan
   const size_t pj = (size_t)p->batch * p->Hq * parts;
   p->off_part_o = off;  off = align_up(off + pj * p->dv * sizeof(float));
   p->off_part_ml = off; off = align_up(off + pj * 2 * sizeof(float));
@@ -223,6 +241,32 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
   return hip_status(launch_select(a, stages, stream));
 }
 
+// Split plan of one attention call: over the selected positions (sparse), all
+// positions (window 0) or the last `window` positions.
+void attend_plan(const Plan& p, bool sparse, int window, int* splits, int* len) {
+  if (p.mla) {
+    if (sparse) {
+      *splits = p.ml_splits;
+      *len = p.ml_len;
+    } else if (window > 0) {
+      mla_dense_plan(std::min<int64_t>(window, p.maxN), p.batch, p.Hq, splits, len);
+    } else {
+      *splits = p.md_splits;
+      *len = p.md_len;
+    }
+    return;
+  }
+  if (sparse) {
+    *splits = p.sp_splits;
+    *len = p.sp_len;
+  } else if (window > 0) {
+    split_plan(std::min<int64_t>(window, p.maxN), p.batch * p.Hkv, splits, len);
+  } else {
+    *splits = p.dn_splits;
+    *len = p.dn_len;
+  }
+}
+
 int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, int window,
                   float sm_scale, uint16_t* out, float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -250,27 +294,9 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
   a.G = p.G;
   a.window = indices ? 0 : window;
   a.parts = p.mla ? 1 : 4;
-  if (p.mla) {
-    if (indices) {
-      a.splits = p.ml_splits;
-      a.split_len = p.ml_len;
-    } else if (window > 0) {
-      mla_dense_plan(std::min<int64_t>(window, p.maxN), p.batch, p.Hq, &a.splits, &a.split_len);
-    } else {
-      a.splits = p.md_splits;
-      a.split_len = p.md_len;
-    }
-    return hip_status(launch_mla_attend(a, stream));
-  }
-  if (indices) {
-    a.splits = p.sp_splits;
-    a.split_len = p.sp_len;
-  } else if (window > 0) {
-    split_plan(std::min<int64_t>(window, p.maxN), p.batch * p.Hkv, &a.splits, &a.split_len);
-  } else {
-    a.splits = p.dn_splits;
-    a.split_len = p.dn_len;
-  }
+  attend_plan(p, indices != nullptr, a.window, &a.splits, &a.split_len);
+  if (a.splits > p.split_cap) return JSSA_ERR_UNSUPPORTED;    // cannot happen (split_capacity)
+  if (p.mla) return hip_status(launch_mla_attend(a, stream));
   return hip_status(launch_attend(a, p.d, stream));
 }
 
@@ -310,6 +336,19 @@ int32_t jssa_decode_path(const jssa_shape* shape, int32_t* single) {
   const bool fits = fused_applies(p.mla, p.d, p.G, p.r, p.maxN, p.B);
   if (shape->select_mode == JSSA_SELECT_FUSED && !fits) return JSSA_ERR_UNSUPPORTED;
   *single = (shape->select_mode == JSSA_SELECT_FUSED || (shape->select_mode == JSSA_SELECT_AUTO && fits)) ? 1 : 0;
+  return JSSA_OK;
+}
+
+int32_t jssa_attend_splits(const jssa_shape* shape, int32_t sparse, int32_t window, int32_t* splits,
+                           int32_t* capacity) {
+  if (!splits || !capacity) return JSSA_ERR_NULL;
+  if (window < 0) return JSSA_ERR_SHAPE;
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  int len = 0;
+  attend_plan(p, sparse != 0, sparse ? 0 : window, splits, &len);
+  *capacity = p.split_cap;
   return JSSA_OK;
 }
 

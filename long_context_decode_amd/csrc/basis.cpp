@@ -3,9 +3,13 @@
 // ("one eigendecomposition per (layer, KV head)").
 //
 // Symmetric eigensolver in double precision: Householder reduction to
-// tridiagonal form with the reflections accumulated into Z, then the QL
-// iteration with implicit Wilkinson-style shifts on the tridiagonal matrix,
-// rotating the columns of Z along.  O(n^3) once per head (n <= 512).
+// tridiagonal form with the reflections accumulated into Z, then the implicit
+// QL algorithm on the tridiagonal matrix, rotating the columns of Z along.
+// The QL step follows the published method of Bowdler, Martin, Reinsch and
+// Wilkinson ("The QR and QL algorithms for symmetric matrices", Numerische
+// Mathematik 11, 1968; the EISPACK routine tql2): a Wilkinson shift from the
+// leading 2 x 2 block, then a chase of plane rotations up the matrix.
+// O(n^3) once per head (n <= 512).
 #include <algorithm>
 #include <cmath>
 #include <limits>

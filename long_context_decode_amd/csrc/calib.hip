@@ -1,7 +1,8 @@
 // jssa_calib_moments: second moments of the calibration group-mean queries and
-// of the keys, per KV head (paper summary page, §3.2 Joint Query-Key Subspace:
-// calibration is second-moment accumulation followed by one eigendecomposition
-// per layer and KV head; README page §2 Calibration).
+// of the keys, per KV head (paper summary page, §3.2 Joint Query-Key Subspace;
+// README page §2 Calibration).  These sums are the only pass over calibration
+// data; the basis then needs a single symmetric eigenproblem per KV head,
+// solved on the host by jssa_basis.
 //
 // Two launches: stage_kernel writes fp32 rows x_t (qbar_t, k_t; MLA: their
 // 512 latent dims) to the workspace; gram_kernel accumulates the d x d sums

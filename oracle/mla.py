@@ -57,11 +57,10 @@ def attend(q_u16: np.ndarray, rows_u16: np.ndarray, sm: float, latent: int = 512
     return o, (mx + np.log(l))[:, 0]
 
 
-def calibrate(q_chunks, latent: int, r: int) -> np.ndarray:
-    """Basis M [1, r, latent] from an iterator of (q [t, Hq, 576], rows [t, 576]) fp64 chunks.
-
-    Second moments of the head-mean query's latent part and of the cached
-    latents, each unit-trace normalised, then Eq. 5."""
+def moments(q_chunks, latent: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(G_Qbar, G_K) [latent, latent] from an iterator of (q [t, Hq, latent+rope], rows [t, latent+rope]) fp64
+    chunks: the uncentred second moments (1/T) sum x x^T of the head-mean query's latent part and of the cached
+    latents c (the RoPE dims are not projected, so they take no part)."""
     sq = sk = None
     n = 0
     for q, rows in q_chunks:
@@ -72,7 +71,14 @@ def calibrate(q_chunks, latent: int, r: int) -> np.ndarray:
         sq = aq if sq is None else sq + aq
         sk = ak if sk is None else sk + ak
         n += q.shape[0]
-    return basis(sq / n, sk / n, r)[None]
+    return sq / n, sk / n
+
+
+def calibrate(q_chunks, latent: int, r: int) -> np.ndarray:
+    """Basis M [1, r, latent]: the moments above, each unit-trace normalised, then Eq. 5 (summary page,
+    Theoretical Foundation; README page §2 Calibration gives the MLA basis shape [1, r, kv_lora_rank])."""
+    gq, gk = moments(q_chunks, latent)
+    return basis(gq, gk, r)[None]
 
 
 def decode_step(q_u16: np.ndarray, rows_u16: np.ndarray, m32: np.ndarray, budget: int, sm: float,
@@ -87,4 +93,5 @@ def decode_step(q_u16: np.ndarray, rows_u16: np.ndarray, m32: np.ndarray, budget
     return dict(codes=codes, scale=scale, qhat=qhat, scores=sc, idx=idx, tau=tau, out=o, lse=lse)
 
 
-__all__ = ["store", "project_query", "attend", "calibrate", "decode_step", "scoring_rows", "second_moment"]
+__all__ = ["store", "project_query", "attend", "moments", "calibrate", "decode_step", "scoring_rows",
+           "second_moment"]

@@ -178,3 +178,49 @@ def test_host_basis_exact_on_known_spectrum():
         v = u[:, i]
         v = v * np.sign(v[np.argmax(np.abs(v))])
         assert np.abs(m[i, :64] - v).max() < 1e-4 and np.abs(m[i, 64:]).max() < 1e-6
+
+
+def _split_shapes():
+    """A seeded sample of GQA and MLA shapes, plus the ones where a window plan takes more splits than the
+    full-capacity plan (129 pages of 16 at batch 8 and 8 KV heads; 257 pages at batch 4 and 8 KV heads)."""
+    rng = np.random.default_rng(11)
+    out = [_shape(batch=8, num_q_heads=32, num_kv_heads=8, max_pages_per_seq=129, budget=256),
+           _shape(batch=4, num_q_heads=8, num_kv_heads=8, max_pages_per_seq=257, budget=1)]
+    for _ in range(60):
+        hkv = int(rng.choice([1, 2, 3, 8]))
+        out.append(_shape(batch=int(rng.integers(1, 17)), num_kv_heads=hkv, num_q_heads=hkv * int(rng.choice([1, 2, 4, 8])),
+                          page_size=int(rng.choice([16, 32, 64])), max_pages_per_seq=int(rng.integers(1, 3000)),
+                          budget=int(rng.integers(1, 4097))))
+    for _ in range(30):
+        out.append(_shape(kind=1, num_kv_heads=1, num_q_heads=int(rng.choice([32, 64, 128])), head_dim=576, rank=64,
+                          batch=int(rng.integers(1, 17)), page_size=int(rng.choice([16, 64])),
+                          max_pages_per_seq=int(rng.integers(1, 3000)), budget=int(rng.integers(1, 4097))))
+    return out
+
+
+def test_attend_splits_fit_the_workspace():
+    """Every attention call's split plan fits the partials the workspace holds: the sparse plan, the dense plan
+    and the plan of every window from 1 to past the capacity (a window rounds its split length to fewer rows
+    than the whole capacity does and can take more splits than the dense plan)."""
+    for sh in _split_shapes():
+        cap_tokens = sh.max_pages_per_seq * sh.page_size
+        sp, cap = L.attend_splits(sh, True)
+        assert 1 <= sp <= cap
+        windows = sorted({1, 2, 255, 256, 257, 2047, 2048, 2049, cap_tokens - 1, cap_tokens, cap_tokens + 5}
+                         | set(range(1, cap_tokens + 1, max(1, cap_tokens // 97))))
+        for win in [0] + [x for x in windows if x > 0]:
+            n, c = L.attend_splits(sh, False, win)
+            assert c == cap and 1 <= n <= cap, (sh.batch, sh.num_kv_heads, sh.max_pages_per_seq, win, n, cap)
+
+
+def test_attend_splits_known_shapes():
+    """The two shapes where the window plan outgrows the full plan: 8 splits of 256 positions for a 2048-token
+    window against 5 of 512 for the whole capacity, and 16 against 9."""
+    sh = _split_shapes()[0]
+    assert L.attend_splits(sh, False, 0)[0] == 5
+    assert L.attend_splits(sh, False, 2048) == (8, 8)
+    sh = _split_shapes()[1]
+    assert L.attend_splits(sh, False, 0)[0] == 9
+    assert L.attend_splits(sh, False, 4096) == (16, 16)
+    with pytest.raises(L.JSSAError):
+        L.attend_splits(sh, False, -1)

@@ -249,10 +249,12 @@ def test_fused_equals_split_sweep(w):
     lay = case.layers[0]
     bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
     rows_k = [ogqa.logical_rows(bf16_bits(lay.k_cache), bt[b], int(sl[b]), w.page_size) for b in range(w.batch)]
+    rows_v = [ogqa.logical_rows(bf16_bits(lay.v_cache), bt[b], int(sl[b]), w.page_size) for b in range(w.batch)]
     assert L.decode_single_launch(L.shape_for(w))
     split = _decode(w, case, m32, rows_k, "fp32", L.SELECT_SPLIT)
     fused = _decode(w, case, m32, rows_k, "fp32", L.SELECT_FUSED)
     _compare(split, fused)
+    _check_oracle(w, case, m32, rows_k, rows_v, "fp32", fused)
 
 
 def test_fused_graph_replay_matches_eager():

@@ -156,3 +156,127 @@ def test_eq2_score_error_identity(tiny_moments):
     eye = np.stack([np.eye(w.head_dim, dtype=np.float32)] * w.num_kv_heads)
     qh = gqa.project_query(q_u16, eye, w.group)
     assert np.allclose(qh[1], q64[w.group:2 * w.group].mean(0), atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- uncentred moments (reading R3)
+
+def test_second_moment_is_uncentred_on_a_hand_example():
+    """Rows (1, 2) and (3, 4): (1/2)[[1+9, 2+12], [2+12, 4+16]] = [[5, 7], [7, 10]].  A centred covariance
+    would be [[1, 1], [1, 1]] (mean (2, 3) removed), so centring anywhere in the chain fails this."""
+    x = np.array([[1.0, 2.0], [3.0, 4.0]])
+    assert np.array_equal(cal.second_moment(x), np.array([[5.0, 7.0], [7.0, 10.0]]))
+    # the per-head moments over a contiguous group: heads 0, 1 -> KV head 0 with qbar = (1, 2) then (3, 4);
+    # keys of KV head 0 are the same rows, so both moments are [[5, 7], [7, 10]]
+    q = np.array([[[0.0, 2.0], [2.0, 2.0]], [[3.0, 5.0], [3.0, 3.0]]])        # [T=2, Hq=2, d=2]
+    k = x[:, None, :]                                                          # [T=2, Hkv=1, d=2]
+    gq, gk = cal.moments_per_head(q, k, 2)
+    assert np.array_equal(gq[0], [[5.0, 7.0], [7.0, 10.0]])
+    assert np.array_equal(gk[0], [[5.0, 7.0], [7.0, 10.0]])
+    sq, sk = cal.moments_streamed([(q[:1], k[:1]), (q[1:], k[1:])], 2)
+    assert np.array_equal(sq, gq) and np.array_equal(sk, gk)
+    # Eq. 3-5 normalisation: each moment divided by its own trace (15), then added
+    a = cal.joint_matrix(gq[0], np.diag([2.0, 2.0]))
+    assert np.allclose(a, np.array([[5.0, 7.0], [7.0, 10.0]]) / 15.0 + np.diag([0.5, 0.5]), atol=1e-15)
+
+
+def test_second_moments_keep_the_mean():
+    """A population with a large mean: the uncentred moment is Sigma + mu mu^T, not Sigma."""
+    rng = np.random.default_rng(21)
+    d, T = 6, 200000
+    mu = np.array([3.0, -2.0, 1.0, 0.0, 0.5, 4.0])
+    x = rng.standard_normal((T, d)) * 0.5 + mu
+    g = cal.second_moment(x)
+    pop = 0.25 * np.eye(d) + np.outer(mu, mu)
+    assert np.abs(g - pop).max() < 0.05
+    assert np.abs(g - 0.25 * np.eye(d)).max() > 10.0
+
+
+# ----------------------------------------------------------------------------- MLA calibration
+
+def _mla_hand_chunks():
+    """latent 2, rope 1, two heads: q rows [t, Hq=2, 3], cached rows [t, 3]."""
+    q = np.array([[[1.0, 1.0, 9.0], [1.0, 3.0, -7.0]],       # head mean latent (1, 2)
+                  [[2.0, 4.0, 5.0], [4.0, 4.0, 5.0]]])        # head mean latent (3, 4)
+    rows = np.array([[1.0, 2.0, 100.0], [3.0, 4.0, -100.0]])  # latent (1, 2), (3, 4); RoPE dim ignored
+    return q, rows
+
+
+def test_mla_moments_hand_example():
+    """Head mean of the latent part of the query and the latent part of the cached rows, uncentred, divided by
+    the token count; the RoPE dims take no part (they are not projected)."""
+    from oracle import mla as omla
+    q, rows = _mla_hand_chunks()
+    want = np.array([[5.0, 7.0], [7.0, 10.0]])
+    gq, gk = omla.moments([(q, rows)], latent=2)
+    assert np.array_equal(gq, want) and np.array_equal(gk, want)
+    # streamed over chunks: the same; changing the RoPE dims changes nothing
+    q2, rows2 = q.copy(), rows.copy()
+    q2[..., 2] = 1e3
+    rows2[:, 2] = -1e3
+    gq2, gk2 = omla.moments([(q2[:1], rows2[:1]), (q2[1:], rows2[1:])], latent=2)
+    assert np.array_equal(gq2, want) and np.array_equal(gk2, want)
+    # the basis is Eq. 5 on those moments: rank 1 of [[5,7],[7,10]]/15 * 2 = the top eigenvector
+    m = omla.calibrate([(q, rows)], latent=2, r=1)
+    lam, vec = np.linalg.eigh(want)
+    v = vec[:, -1] * np.sign(vec[np.argmax(np.abs(vec[:, -1])), -1])
+    assert m.shape == (1, 1, 2)
+    assert np.allclose(m[0, 0], v, atol=1e-14)
+
+
+@pytest.fixture(scope="module")
+def mla_moments():
+    """The tiny MLA workload's calibration set (1024 tokens, 128 heads, 512 + 64 dims) in fp64."""
+    from oracle import mla as omla
+    from synth import make_mla_calibration
+    w = WORKLOADS["tiny_mla"]
+    chunks = [(cal.bf16_to_f64(bf16_bits(q)), cal.bf16_to_f64(bf16_bits(l)))
+              for q, l in make_mla_calibration(w, chunk=512)]
+    gq, gk = omla.moments(chunks, w.latent_dim)
+    return w, chunks, gq, gk
+
+
+def test_mla_moments_match_population(mla_moments):
+    """Cached latents c = U diag(i^-0.8) z: E[c c^T] = U diag(i^-1.6) U^T; the head mean of Hq independent
+    query heads amp U diag(i^-0.5) z': E = (amp^2 / Hq) U diag(i^-1) U^T.  Sample deviation as in the GQA pin."""
+    import math
+    from synth.workloads import _haar_cached, P_BASIS
+    w, _, gq, gk = mla_moments
+    dl, dr = w.latent_dim, w.rope_dim
+    u = _haar_cached(w.model, 0, 0, dl, P_BASIS)
+    tot = float(np.sum(np.arange(1, dl + 1, dtype=np.float64) ** -2.6) +
+                np.sum(np.arange(1, dr + 1, dtype=np.float64) ** -2.6))
+    amp = math.sqrt((128 + dr) / tot)
+    pop_k = (u * key_spectrum(dl) ** 2) @ u.T
+    pop_q = (u * (amp ** 2 / w.num_q_heads) * query_spectrum(dl) ** 2) @ u.T
+    T = w.calib_seqs * w.calib_len
+    for g_hat, pop in ((gk, pop_k), (gq, pop_q)):
+        rel = np.linalg.norm(g_hat - pop) / np.linalg.norm(pop)
+        expect = np.sqrt((np.trace(pop) ** 2 + np.linalg.norm(pop) ** 2) / T) / np.linalg.norm(pop)
+        assert 0.5 * expect < rel < 1.5 * expect, (rel, expect)
+
+
+def test_mla_basis_orthonormal_ky_fan_and_eq4(mla_moments):
+    """The MLA basis: orthonormal rows (also in fp32), L_marg equal to the sum of the discarded eigenvalues of
+    the normalised moment sum and no larger than that of 200 Haar-random rank-r projectors, Eq. 4 on its
+    projector, and the same basis from any chunking of the calibration set."""
+    from oracle import mla as omla
+    w, chunks, gq, gk = mla_moments
+    dl, r = w.latent_dim, w.rank
+    m = omla.calibrate(iter(chunks), dl, r)[0]
+    assert m.shape == (r, dl)
+    assert np.abs(m @ m.T - np.eye(r)).max() < 1e-12
+    m32 = m.astype(np.float32).astype(np.float64)
+    assert np.abs(m32 @ m32.T - np.eye(r)).max() < 1e-6
+    lam = np.sort(np.linalg.eigvalsh(cal.joint_matrix(gq, gk)))[::-1]
+    p = cal.projector(m)
+    best = cal.l_marg(p, gq, gk)
+    assert abs(best - lam[r:].sum()) < 1e-12
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        assert cal.l_marg(_haar_projector(dl, r, rng), gq, gk) >= best - 1e-12
+    assert cal.l_sel(p, gq, gk) <= 0.25 * best ** 2 + 1e-14
+    # one chunk of 1024 against two of 512
+    q_all = np.concatenate([c[0] for c in chunks])
+    r_all = np.concatenate([c[1] for c in chunks])
+    m_one = omla.calibrate([(q_all, r_all)], dl, r)[0]
+    assert np.abs(np.abs(np.sum(m_one * m, axis=1)) - 1.0).max() < 1e-9

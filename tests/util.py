@@ -42,6 +42,27 @@ def check_codes(gpu_codes, orc_codes, max_frac=1e-3):
     return frac
 
 
+class CodeTally:
+    """FP8 store parity counted over every code a test compares: each entry within 1 ulp (signed-magnitude
+    distance), and the differing entries at most max_frac (0.1 %) of all entries compared in the test, not
+    of one row (a row of 32 codes cannot express 0.1 %)."""
+
+    def __init__(self):
+        self.diff = 0
+        self.total = 0
+
+    def add(self, gpu_codes, orc_codes):
+        d = np.abs(fp8.signed_magnitude(gpu_codes) - fp8.signed_magnitude(orc_codes))
+        assert d.max(initial=0) <= 1, f"code distance {d.max()} ulp"
+        self.diff += int((d > 0).sum())
+        self.total += int(d.size)
+
+    def check(self, max_frac=1e-3):
+        assert self.total > 0
+        assert self.diff <= max_frac * self.total, f"{self.diff} of {self.total} codes differ"
+        return self.diff
+
+
 def check_selection(gpu_idx, orc_idx, orc_scores, tau, rel=1e-5):
     """Selected sets equal except tokens whose oracle score is within rel*|tau| of the B-th score.
 
