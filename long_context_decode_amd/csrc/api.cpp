@@ -27,7 +27,7 @@ struct Plan {
   int md_splits, md_len;     // MLA dense (window 0) split plan
   int stage_pages;            // gather-then-attend staging cache: pages per sequence
   int split_cap;              // splits the workspace's partials hold per (sequence, query head)
-  size_t off_qhat, off_tau, off_chunk, off_cand, off_part_o, off_part_ml;
+  size_t off_qhat, off_tau, off_cand, off_part_o, off_part_ml;
   size_t off_stage_k, off_stage_v, off_stage_table, off_stage_lens, total;
 };
 
@@ -145,11 +145,10 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   if (p->mla) mla_dense_plan((int64_t)p->stage_pages * p->P, p->batch, p->Hq, &st_splits, &st_len);
   else split_plan((int64_t)p->stage_pages * p->P, p->batch * p->Hkv, &st_splits, &st_len);
   const size_t bh = (size_t)p->batch * p->Hkv;
-  const size_t cand = bh * p->max_chunks * p->cp * p->P;   // one region per stream chunk
+  const size_t cand = bh * p->max_chunks * (size_t)(p->cp * p->P + kRegionPad);   // one region per stream chunk
   size_t off = 0;
   p->off_qhat = off;    off = align_up(off + bh * p->S * sizeof(float));
   p->off_tau = off;     off = align_up(off + bh * sizeof(uint32_t));
-  p->off_chunk = off;   off = align_up(off + bh * p->max_chunks * sizeof(int32_t));
   p->off_cand = off;    off = align_up(off + cand * 2 * sizeof(uint32_t));
   // split-K partials: one per block for MLA, one per wavefront (4 per split)
   // for GQA.  Sized for the most splits any plan of this shape can take: a
@@ -220,7 +219,6 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
   a.scores_out = scores_out;
   a.qhat = at<float>(ws, p.off_qhat);
   a.tau = at<uint32_t>(ws, p.off_tau);
-  a.chunk_cnt = at<int32_t>(ws, p.off_chunk);
   a.k_new = k_new;
   a.slot_new = slot_new;
   a.cand = at<uint2>(ws, p.off_cand);
@@ -237,6 +235,7 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
   a.mla = p.mla;
   a.cp = p.cp;
   a.max_chunks = p.max_chunks;
+  a.reg_len = p.cp * p.P + kRegionPad;
   a.force_exact = select_mode == JSSA_SELECT_EXACT_STREAM;
   return hip_status(launch_select(a, stages, stream));
 }

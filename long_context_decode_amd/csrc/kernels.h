@@ -10,6 +10,7 @@ namespace jssa {
 constexpr int kCandCap = 12288;       // candidates the finish kernel holds in LDS per (sequence, KV head)
 constexpr int kSampleMax = 8192;      // sampled tokens per (sequence, KV head)
 constexpr int kMaxChunks = 4096;      // stream chunks per sequence the finish kernel can order
+constexpr int kRegionPad = 16;        // a candidate region holds one chunk's tokens plus one 128-byte line
 constexpr int kMlaLatent = 512;
 constexpr int kMlaRope = 64;
 
@@ -35,8 +36,9 @@ struct SelectArgs {
   // workspace
   float* qhat;          // [batch, Hkv, S]
   uint32_t* tau;        // [batch, Hkv]
-  int32_t* chunk_cnt;   // [batch, Hkv, max_chunks] candidates found by each chunk
-  uint2* cand;          // [batch, Hkv, max_chunks, cp * P] (key, position), one region per chunk
+  uint2* cand;          // [batch, Hkv, max_chunks, reg_len]: per chunk a header entry (x = count), then
+                        // the chunk's (key, position) candidates in position order
+  int reg_len;          // entries per region: cp * P + kRegionPad
   // new-token store fused into the prologue (k_new == NULL: none)
   const uint16_t* k_new;
   const int32_t* slot_new;

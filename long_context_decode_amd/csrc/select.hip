@@ -16,8 +16,9 @@
 //     all pages at once with streaming (non-temporal) loads, since each
 //     byte is read once per step (a wavefront reads one contiguous run per
 //     piece), scores them, and the keys >= tau are compacted in position
-//     order straight from the ballot masks into the chunk's region of the
-//     candidate buffer; the chunk's count is recorded.
+//     order from the ballot masks into LDS; each (chunk, KV head) region of
+//     the candidate buffer then goes out as whole 128-byte lines, a header
+//     entry holding the count followed by the candidates.
 //  3. finish    (one 1024-thread block per (sequence, KV head)): gathers the
 //     candidates into LDS in chunk order (so they are in position order),
 //     radix-selects the B-th largest key, and writes the winners ascending
@@ -342,7 +343,9 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int RP = TokenPieces<R, BF>::value;
   constexpr int HPW = 64 / P;               // KV heads covered by one wavefront
   constexpr int PF = RP >= 16 ? 1 : 16 / RP;  // pages of a wavefront (all in flight at once)
+  constexpr int RL = 4 * PF * P + kRegionPad; // entries of one (chunk, KV head) region
   __shared__ uint32_t wcnt[4][HPW];
+  __shared__ __align__(16) uint2 stage[HPW * 4 * PF * P];   // [head][wavefront][PF * P]
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
   const int hg = blockIdx.x, c = blockIdx.y, b = blockIdx.z;   // chunk c = 4 wavefronts
   const int N = seq_len_of(a, b);
@@ -383,40 +386,50 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
   const int64_t maxN = (int64_t)a.max_pages * P;
   float* sout = a.scores_out ? a.scores_out + bh * maxN : nullptr;
 
-  // keys and ballot masks of every page of the wavefront
-  uint32_t key[PF];
-  uint64_t mask[PF];
+  // each page's keys >= tau go, in position order, to this wavefront's part of
+  // the LDS staging area of its KV head (right after the ballot: no key or mask
+  // stays live across the block barrier)
   const uint64_t hmask = (P == 64) ? ~0ull : (((1ull << (P & 63)) - 1ull) << (hl * P));
+  uint2* st = stage + (hl * 4 + w) * (PF * P);
   uint32_t cnt = 0;
 #pragma unroll
   for (int f = 0; f < PF; ++f) {
     const int t = (page0 + f) * P + slot;
-    key[f] = 0u;
+    uint32_t key = 0u;
     if (any && active && t < N) {
       const float s = score_token<R, BF>(pc[f], qh) * sc[f];
-      key[f] = score_key(s);
+      key = score_key(s);
       if (sout) sout[t] = s;
     }
-    mask[f] = ballot(key[f] >= tau) & hmask;
-    cnt += (uint32_t)__popcll(mask[f]);
+    const uint64_t m = ballot(key >= tau) & hmask;
+    if (m & (1ull << lane)) st[cnt + lanes_below(m)] = make_uint2(key, (uint32_t)t);
+    cnt += (uint32_t)__popcll(m);
   }
-  // the block's four wavefronts share one region: offsets from their counts
   if (slot == 0) wcnt[w][hl] = cnt;
   __syncthreads();
-  uint32_t run = 0, total = 0;
+  // every region goes out as whole 128-byte lines: a header entry (x = the
+  // chunk's count), then the four wavefronts' candidates in wavefront order
+  // (= position order), the tail of the last line padded (scattered
+  // partial-line stores of the candidates measured 6.8 us slower at 128K)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const uint32_t x = wcnt[v][hl];
-    run += v < w ? x : 0u;
-    total += x;
-  }
-  if (w == 0 && slot == 0 && active) a.chunk_cnt[bh * a.max_chunks + c] = (int32_t)total;
-  uint2* region = a.cand + (bh * a.max_chunks + c) * (int64_t)(a.cp * P);
-#pragma unroll
-  for (int f = 0; f < PF; ++f) {
-    const uint64_t m = mask[f];
-    if (m & (1ull << lane)) region[run + lanes_below(m)] = make_uint2(key[f], (uint32_t)((page0 + f) * P + slot));
-    run += (uint32_t)__popcll(m);
+  for (int h = 0; h < HPW; ++h) {
+    const int hh = hg * HPW + h;
+    if (hh >= a.Hkv) break;                    // uniform
+    const uint32_t n0 = wcnt[0][h], n1 = wcnt[1][h], n2 = wcnt[2][h], n3 = wcnt[3][h];
+    const uint32_t o1 = n0, o2 = o1 + n1, o3 = o2 + n2, n = o3 + n3;
+    const int len = (int)((n + 16) & ~15u);    // header + n entries, whole lines
+    uint2* dst = a.cand + (((int64_t)b * a.Hkv + hh) * a.max_chunks + c) * RL;
+    const uint2* sh = stage + h * 4 * (PF * P);
+    for (int e = (int)threadIdx.x; e < len; e += kStreamThreads) {
+      const uint32_t k = (uint32_t)e - 1u;
+      uint2 v = make_uint2(n, 0u);
+      if (e > 0) {
+        const int wv = k >= o3 ? 3 : (k >= o2 ? 2 : (k >= o1 ? 1 : 0));
+        const uint32_t ov = wv == 3 ? o3 : (wv == 2 ? o2 : (wv == 1 ? o1 : 0u));
+        v = k < n ? sh[wv * (PF * P) + (k - ov)] : make_uint2(0u, 0u);
+      }
+      dst[e] = v;
+    }
   }
 }
 
@@ -491,23 +504,23 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   const uint32_t tau = a.tau[bh];
   const int n_pages = (N + a.P - 1) / a.P;
   const int n_chunks = (n_pages + a.cp - 1) / a.cp;
-  // chunk offsets in chunk (= position) order
-  const int32_t* cnts = a.chunk_cnt + bh * a.max_chunks;
-  const int cap_chunk = a.cp * a.P;
-  // the count of chunk tid and the first 16 entries of its region (a region
-  // holds at least 64) are requested together, before the count scan
+  // chunk offsets in chunk (= position) order.  A region is a header entry
+  // (x = the chunk's count) followed by its candidates; the first line of
+  // region tid (header + 15 candidates) is requested before the count scan
+  const int rl = a.reg_len;
+  const uint2* regions = a.cand + bh * a.max_chunks * (int64_t)rl;
   const bool pact = !a.force_exact && tid < n_chunks;
-  const uint32_t cnt0 = pact ? (uint32_t)cnts[tid] : 0u;
   uint4 pre[8];
   if (pact) {
-    const uint4* src = reinterpret_cast<const uint4*>(a.cand + (bh * a.max_chunks + tid) * (int64_t)cap_chunk);
+    const uint4* src = reinterpret_cast<const uint4*>(regions + (int64_t)tid * rl);
 #pragma unroll
     for (int j = 0; j < 8; ++j) pre[j] = src[j];
   }
+  const uint32_t cnt0 = pact ? pre[0].x : 0u;
   uint32_t carry = 0;
   for (int c0 = 0; c0 < n_chunks && !a.force_exact; c0 += kFinishThreads) {
     const int c = c0 + tid;
-    const uint32_t cnt = c0 == 0 ? cnt0 : (c < n_chunks ? (uint32_t)cnts[c] : 0u);
+    const uint32_t cnt = c0 == 0 ? cnt0 : (c < n_chunks ? regions[(int64_t)c * rl].x : 0u);
     uint32_t tot;
     const uint32_t ex = block_excl_scan<kFinishThreads>(cnt, tmp, &tot);
     if (c < n_chunks) coff[c] = carry + ex;
@@ -524,13 +537,13 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
   }
   if (tid == 0) coff[n_chunks] = carry;
   __syncthreads();
-  // gather the candidates in position order: thread c copies the first 16
-  // entries of chunk c's contiguous run to its offset (read unconditionally,
-  // prefetched for c = tid)
+  // gather the candidates in position order: thread c copies the first 15
+  // candidates of chunk c (entries 1..15 of its region) to its offset (read
+  // unconditionally, prefetched for c = tid)
   {
     for (int c = tid; c < n_chunks; c += kFinishThreads) {
       const int cnt = (int)(coff[c + 1] - coff[c]);
-      const uint2* src = a.cand + (bh * a.max_chunks + c) * (int64_t)cap_chunk;
+      const uint2* src = regions + (int64_t)c * rl;
       const uint32_t dst = coff[c];
       uint4 v[8];
       if (c == tid) {
@@ -542,13 +555,14 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (2 * j < cnt) {
-          lkey[dst + 2 * j] = v[j].x;
-          lidx[dst + 2 * j] = (int32_t)v[j].y;
+        // entries 2j and 2j + 1 are candidates 2j - 1 and 2j
+        if (j > 0 && 2 * j - 1 < cnt) {
+          lkey[dst + 2 * j - 1] = v[j].x;
+          lidx[dst + 2 * j - 1] = (int32_t)v[j].y;
         }
-        if (2 * j + 1 < cnt) {
-          lkey[dst + 2 * j + 1] = v[j].z;
-          lidx[dst + 2 * j + 1] = (int32_t)v[j].w;
+        if (2 * j < cnt) {
+          lkey[dst + 2 * j] = v[j].z;
+          lidx[dst + 2 * j] = (int32_t)v[j].w;
         }
       }
     }
@@ -560,9 +574,9 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
     const int cpw = 64 / lpc, sub = lane % lpc;
     for (int c = w * cpw + lane / lpc; c < n_chunks; c += (kFinishThreads / 64) * cpw) {
       const int cnt = (int)(coff[c + 1] - coff[c]);
-      const uint2* src = a.cand + (bh * a.max_chunks + c) * (int64_t)cap_chunk;
+      const uint2* src = regions + (int64_t)c * rl + 1;    // candidate i at entry 1 + i
       const uint32_t dst = coff[c];
-      for (int i0 = 16 + sub; i0 < cnt; i0 += 4 * lpc) {
+      for (int i0 = 15 + sub; i0 < cnt; i0 += 4 * lpc) {
         uint2 e[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) e[k] = src[i0 + k * lpc < cnt ? i0 + k * lpc : i0];
