@@ -206,7 +206,9 @@ int32_t jssa_select_stages(const jssa_shape* shape, int32_t stages, const uint16
  * [batch, Hq, 512] (v_cache ignored, may be NULL).  lse_out (optional, fp32
  * [batch, Hq], natural log) receives log sum exp of the logits.  An empty set
  * gives out = 0 and lse = -inf.
- * indices : int32 [batch, Hkv, B] as written by jssa_select (-1 entries skipped). */
+ * indices : int32 [batch, Hkv, B] as written by jssa_select; an entry outside
+ *           [0, seq_lens[b]) (such as the -1 padding) is skipped, so a bad
+ *           index drops a position instead of reading outside the caches. */
 int32_t jssa_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
                     const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                     const int32_t* indices, float sm_scale, uint16_t* out, float* lse_out,

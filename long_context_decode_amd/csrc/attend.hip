@@ -195,11 +195,12 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   const int32_t* idx = DENSE ? nullptr : a.indices + ((int64_t)b * a.Hkv + h) * a.B;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  // lane -> slot index (physical page * P + slot) of position ii, or -1
+  // lane -> slot index (physical page * P + slot) of position ii, or -1 (a
+  // listed position outside [0, N) counts as missing)
   auto slot_of = [&](int ii) -> int {
     if (ii >= i1) return -1;
     const int t = DENSE ? lo + ii : idx[ii];
-    return t >= 0 ? bt[t / a.P] * a.P + (t % a.P) : -1;
+    return (t >= 0 && t < N) ? bt[t / a.P] * a.P + (t % a.P) : -1;
   };
   int ri = slot_of(i0 + w * 64 + lane);
   for (int base = i0 + w * 64; base < i1; base += 256) {

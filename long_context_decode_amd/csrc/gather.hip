@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     int s = -1;
     if (tid < n) {
       const int t = a.indices[((int64_t)b * a.Hkv + h) * a.B + i0 + tid];
-      if (t >= 0) s = a.block_table[(int64_t)b * a.max_pages + t / a.P] * a.P + t % a.P;
+      if (t >= 0 && t < N) s = a.block_table[(int64_t)b * a.max_pages + t / a.P] * a.P + t % a.P;
     }
     src[tid] = s;
   }

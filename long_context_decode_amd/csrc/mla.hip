@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int j = 0; j < kChunkRows / kThreads; ++j) {
       const int ii = base + tid + j * kThreads;
       tv[j] = idx[ii < i1 ? ii : i1 - 1];
-      if (ii >= i1) tv[j] = -1;
+      if (ii >= i1 || tv[j] >= N) tv[j] = -1;     // a listed position outside [0, N) counts as missing
     }
 #pragma unroll
     for (int j = 0; j < kChunkRows / kThreads; ++j) pv[j] = bt[(tv[j] < 0 ? 0 : tv[j]) / a.P];

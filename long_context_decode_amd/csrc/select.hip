@@ -516,11 +516,14 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) pre[j] = src[j];
   }
-  const uint32_t cnt0 = pact ? pre[0].x : 0u;
+  // (a count is at most the chunk's tokens; the clamp keeps every read inside
+  // the region whatever the header holds)
+  const uint32_t cap_chunk = (uint32_t)(a.cp * a.P);
+  const uint32_t cnt0 = pact ? min(pre[0].x, cap_chunk) : 0u;
   uint32_t carry = 0;
   for (int c0 = 0; c0 < n_chunks && !a.force_exact; c0 += kFinishThreads) {
     const int c = c0 + tid;
-    const uint32_t cnt = c0 == 0 ? cnt0 : (c < n_chunks ? regions[(int64_t)c * rl].x : 0u);
+    const uint32_t cnt = c0 == 0 ? cnt0 : (c < n_chunks ? min(regions[(int64_t)c * rl].x, cap_chunk) : 0u);
     uint32_t tot;
     const uint32_t ex = block_excl_scan<kFinishThreads>(cnt, tmp, &tot);
     if (c < n_chunks) coff[c] = carry + ex;
