@@ -7,24 +7,13 @@
 // keep dense attention).
 //
 // Block = (split, KV head, sequence), 4 wavefronts; a wavefront takes 64
-// positions at a time ("batch"), lane i resolving position i to its K/V row
-// through the block table.  Row r of 16 lanes handles positions 16r..16r+15,
-// one per iteration; a lane holds D/16 elements of the row, 8 contiguous ones
-// of each 128-dim block (one 16-byte load per block, so that a load
-// instruction covers 256 contiguous bytes of the row).  Per batch:
-//   A. the K rows are requested 16 (d = 128) or 8 (d = 256) at a time, then
-//      q.k is formed with v_dot2_f32_bf16 on the bf16 pairs and summed over
-//      the row with DPP; every position's logit (base 2, scaled by
-//      sm * log2 e) lands in the lane that owns the position;
-//   B. one softmax update per batch: the wave max of the 64 logits, a single
-//      rescale of the running state, p = 2^(x - m) per lane;
-//   C. the V rows are requested 8 (d = 128) or 4 (d = 256) at a time and
-//      o += p v, p broadcast along the row with DPP (row_newbcast).
-// Each loaded row serves all G query heads of the KV head.  The running max is
-// uniform over the wavefront, so the rows' partial sums add directly; each
+// positions at a time, lane i resolving position i to its K/V row through the
+// block table, and runs the batch of attend_core.h (K rows, one softmax update,
+// V rows; each loaded row serves all G query heads of the KV head).  Each
 // wavefront writes its own partial (o, m, l), and merge_kernel combines them.
 // DENSE instantiates the full-KV / sliding-window baseline (positions [lo, N)
 // instead of an index list).
+#include "attend_core.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -131,23 +120,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttendArgs a) {
   if (tid == 0 && a.lse_out) a.lse_out[(int64_t)b * a.Hq + j] = L > 0.0f ? (mm + log2f(L)) * kLn2 : -INFINITY;
 }
 
-// 16 bytes of a K or V row; the full-cache scan reads every row once, so its
-// loads are streaming (non-temporal) ones
-template <bool STREAM>
-__device__ __forceinline__ uint4 load_row_piece(const uint16_t* p) {
-  return STREAM ? load_stream_u4(p) : *reinterpret_cast<const uint4*>(p);
-}
-
 // Lane (row, c16) of a wavefront holds dims 128 v + 8 c16 ... 128 v + 8 c16 + 7
 // (v < D / 128) of the query, the K and V rows and the output, so that each
 // 16-byte load instruction covers 256 contiguous bytes of a row.
 template <int D, int G, bool DENSE>
 __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
-  constexpr int EPL = D / 16;   // elements per lane
-  constexpr int NV = EPL / 8;   // 16-byte loads per lane per row
-  constexpr int NP = EPL / 2;   // bf16 pairs per lane per row
-  constexpr int GRP = 8 / NV;   // V rows whose loads are in flight together (32 VGPRs)
-  constexpr int GRPK = 16 / NV; // K rows whose loads are in flight together (64 VGPRs)
+  constexpr int EPL = AttendShape<D>::EPL, NP = AttendShape<D>::NP;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = (int)threadIdx.x, lane = lane_id(), w = tid >> 6;
   const int row = lane >> 4, c16 = lane & 15;
@@ -166,28 +144,10 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   if (i0 >= n_tok) return;
   const int i1 = min(i0 + a.split_len, n_tok);
 
-  // query heads of this KV head as bf16 pairs (unscaled; the scale is applied to the row sums)
   uint32_t qp[G][NP];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint16_t* q = a.q + ((int64_t)b * a.Hq + (int64_t)h * G + g) * D + c16 * 8;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const uint4 u = *reinterpret_cast<const uint4*>(q + v * 128);
-      qp[g][4 * v] = u.x;
-      qp[g][4 * v + 1] = u.y;
-      qp[g][4 * v + 2] = u.z;
-      qp[g][4 * v + 3] = u.w;
-    }
-  }
+  load_query_pairs<D, G>(a.q + ((int64_t)b * a.Hq + (int64_t)h * G) * D, c16, qp);
   float m[G], l[G], o[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
-  }
+  attend_state_init<D, G>(m, l, o);
 
   const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive token slots
   const uint16_t* kbase = a.k_cache + (int64_t)h * D + c16 * 8;
@@ -206,104 +166,14 @@ __global__ __launch_bounds__(kAttendThreads) void attend_kernel(AttendArgs a) {
   for (int base = i0 + w * 64; base < i1; base += 256) {
     // the next batch's slots are resolved while this batch is in flight
     const int ri_next = slot_of(base + 256 + lane);
-    // ---- A: logits of the 64 positions (row r, iteration u -> position 16r + u)
-    float xs[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) xs[g] = -INFINITY;
-#pragma unroll
-    for (int u0 = 0; u0 < 16; u0 += GRPK) {
-      uint4 kr[GRPK][NV];
-#pragma unroll
-      for (int u = 0; u < GRPK; ++u) {
-        const int rr = row_bcast(ri, u0 + u);
-        const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) kr[u][v] = load_row_piece<DENSE>(kbase + ro + v * 128);
-      }
-#pragma unroll
-      for (int u = 0; u < GRPK; ++u) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = 0.0f;
-#pragma unroll
-          for (int v = 0; v < NV; ++v) {
-            acc = dot2_bf16(kr[u][v].x, qp[g][4 * v], acc);
-            acc = dot2_bf16(kr[u][v].y, qp[g][4 * v + 1], acc);
-            acc = dot2_bf16(kr[u][v].z, qp[g][4 * v + 2], acc);
-            acc = dot2_bf16(kr[u][v].w, qp[g][4 * v + 3], acc);
-          }
-          const float x = row16_sum(acc) * a.sm_log2;
-          if (c16 == u0 + u) xs[g] = x;
-        }
-      }
-    }
-    if (ri < 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) xs[g] = -INFINITY;
-    }
-    // ---- B: one softmax update for the batch
-    float p[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mn = fmaxf(m[g], wave_max(xs[g]));
-      if (mn > m[g]) {                     // uniform over the wavefront
-        const float al = __builtin_amdgcn_exp2f(m[g] - mn);
-        l[g] *= al;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[g][e] *= al;
-        m[g] = mn;
-      }
-      p[g] = (m[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(xs[g] - m[g]);
-      l[g] += p[g];
-    }
-    // ---- C: o += p v over the 64 rows
-#pragma unroll
-    for (int u0 = 0; u0 < 16; u0 += GRP) {
-      uint4 vr[GRP][NV];
-#pragma unroll
-      for (int u = 0; u < GRP; ++u) {
-        const int rr = row_bcast(ri, u0 + u);
-        const int64_t ro = (int64_t)(rr < 0 ? 0 : rr) * row_stride;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) vr[u][v] = load_row_piece<DENSE>(vbase + ro + v * 128);
-      }
-#pragma unroll
-      for (int u = 0; u < GRP; ++u) {
-        float pp[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) pp[g] = row_bcast_f(p[g], u0 + u);
-        // a missing position's row is read from slot 0: its weight is 0, and
-        // its values are zeroed so that whatever slot 0 holds adds nothing
-        const bool ok = row_bcast(ri, u0 + u) >= 0;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          const uint4 vv = vr[u][v];
-          const uint32_t ww[4] = {ok ? vv.x : 0u, ok ? vv.y : 0u, ok ? vv.z : 0u, ok ? vv.w : 0u};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v0 = bf16_lo(ww[e]), v1 = bf16_hi(ww[e]);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-              o[g][v * 8 + 2 * e] = __builtin_fmaf(pp[g], v0, o[g][v * 8 + 2 * e]);
-              o[g][v * 8 + 2 * e + 1] = __builtin_fmaf(pp[g], v1, o[g][v * 8 + 2 * e + 1]);
-            }
-          }
-        }
-      }
-    }
+    attend_batch<D, G, DENSE>(kbase, vbase, row_stride, ri, qp, a.sm_log2, c16, m, l, o);
     ri = ri_next;
   }
 
-  // rows share the wave's running max: sum the four rows and the lanes' l,
-  // then this wavefront's partial (o, m, l) goes out as partial 4 s + w
+  // this wavefront's partial (o, m, l) goes out as partial 4 s + w
+  wave_state_sum<D, G>(l, o);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    l[g] = wave_sum(l[g]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      o[g][e] += __shfl_xor(o[g][e], 16);
-      o[g][e] += __shfl_xor(o[g][e], 32);
-    }
     const int64_t pj = ((int64_t)b * a.Hq + (int64_t)h * G + g) * ((int64_t)a.splits * 4) + s * 4 + w;
     if (row == 0) {
 #pragma unroll
