@@ -20,7 +20,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Plan {
   int kind, batch, Hq, Hkv, d, P, max_pages, r, S, B, G, mla, dv, sfmt;
   int64_t maxN;
-  int cp, max_chunks;
+  int cp, max_chunks, heads_pb, chunks_pb;
   int sp_splits, sp_len;     // sparse attention split plan
   int dn_splits, dn_len;     // dense (window 0) split plan
   int ml_splits, ml_len;     // MLA sparse attention split plan
@@ -122,10 +122,12 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   p->G = p->Hq / p->Hkv;
   p->dv = p->mla ? kMlaLatent : p->d;
   p->maxN = (int64_t)p->max_pages * p->P;
-  // stream chunking: one wavefront per chunk of 4 groups of 16 / (S / 16) pages
-  // stream chunk: 4 wavefronts x 16 / (16-byte pieces per token) pages
+  // stream chunk: the pages one wavefront scores for one KV head, 64 / P pages
+  // per round and 16 / (16-byte pieces per token) rounds
   const int pieces = (p->sfmt == JSSA_KEYS_BF16 ? 2 : 1) * (p->S / 16);
-  p->cp = 4 * std::max(1, 16 / pieces);
+  p->cp = (64 / p->P) * std::max(1, 16 / pieces);
+  p->heads_pb = std::min(p->Hkv, kStreamWaves);
+  p->chunks_pb = kStreamWaves / p->heads_pb;
   p->max_chunks = (int)cdiv(p->max_pages, p->cp);
   if (p->max_chunks > kMaxChunks) return JSSA_ERR_UNSUPPORTED;
   split_plan(std::min<int64_t>(p->B, p->maxN), p->batch * p->Hkv, &p->sp_splits, &p->sp_len);
@@ -235,6 +237,8 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
   a.mla = p.mla;
   a.cp = p.cp;
   a.max_chunks = p.max_chunks;
+  a.heads_pb = p.heads_pb;
+  a.chunks_pb = p.chunks_pb;
   a.reg_len = p.cp * p.P + kRegionPad;
   a.force_exact = select_mode == JSSA_SELECT_EXACT_STREAM;
   return hip_status(launch_select(a, stages, stream));

@@ -9,8 +9,9 @@ namespace jssa {
 
 constexpr int kCandCap = 12288;       // candidates the finish kernel holds in LDS per (sequence, KV head)
 constexpr int kSampleMax = 8192;      // sampled tokens per (sequence, KV head)
-constexpr int kMaxChunks = 4096;      // stream chunks per sequence the finish kernel can order
+constexpr int kMaxChunks = 8192;      // stream chunks per sequence the finish kernel can order
 constexpr int kRegionPad = 16;        // a candidate region holds one chunk's tokens plus one 128-byte line
+constexpr int kStreamWaves = 4;       // wavefronts of a score-stream block
 constexpr int kMlaLatent = 512;
 constexpr int kMlaRope = 64;
 
@@ -43,8 +44,10 @@ struct SelectArgs {
   const uint16_t* k_new;
   const int32_t* slot_new;
   int batch, Hq, Hkv, d, P, max_pages, r, S, B, G, mla;
-  int cp;               // pages per stream chunk (4 groups of 16 / (scoring dims / 16))
+  int cp;               // pages per stream chunk: the pages one wavefront scores (16 / pieces rounds of 64 / P)
   int max_chunks;
+  int heads_pb, chunks_pb;  // stream block: wavefront w scores KV head w % heads_pb of the block's head
+                            // group over chunk w / heads_pb of its chunk group (heads_pb * chunks_pb <= 4)
   int force_exact;
   int sfmt;             // 0 fp32 scale, 1 E8M0 byte, 2 none
 };

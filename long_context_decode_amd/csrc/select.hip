@@ -9,16 +9,17 @@
 //     sample of the sequence's pages and picks a threshold key tau that about
 //     2B tokens should clear (tau = "all" when the whole sequence fits the
 //     candidate buffer).  In jssa_decode it also stores the new token.
-//  2. stream    (each wavefront owns 16/R consecutive pages of one sequence
-//     for a group of KV heads; a block's four wavefronts form one chunk):
-//     every lane owns one (KV head, slot) and reads that token's 16-byte
-//     pieces (FP8 codes, or BF16 keys: twice the pieces, half the pages) for
-//     all pages at once with streaming (non-temporal) loads, since each
-//     byte is read once per step (a wavefront reads one contiguous run per
-//     piece), scores them, and the keys >= tau are compacted in position
-//     order from the ballot masks into LDS; each (chunk, KV head) region of
-//     the candidate buffer then goes out as whole 128-byte lines, a header
-//     entry holding the count followed by the candidates.
+//  2. stream    (a wavefront scores one chunk of consecutive pages for one
+//     KV head; the four wavefronts of a block take four KV heads of the same
+//     pages, or, with fewer KV heads, consecutive chunks): lane = (page of the
+//     round, slot), and every lane reads its token's 16-byte pieces (FP8
+//     codes, or BF16 keys: twice the pieces) for all rounds at once with
+//     streaming (non-temporal) loads, since each byte is read once per step;
+//     the head's projected query sits in scalar registers.  The keys >= tau
+//     are compacted in position order from the ballot masks into the
+//     wavefront's LDS area, and its (chunk, KV head) region of the candidate
+//     buffer goes out as whole 128-byte lines: a header entry holding the
+//     count, then the candidates.  No block barrier.
 //  3. finish    (one 1024-thread block per (sequence, KV head)): gathers the
 //     candidates into LDS in chunk order (so they are in position order),
 //     radix-selects the B-th largest key, and writes the winners ascending
@@ -37,7 +38,7 @@ namespace {
 
 constexpr int kPrologueThreads = 1024;
 constexpr int kFinishThreads = 1024;
-constexpr int kStreamThreads = 256;
+constexpr int kStreamThreads = 64 * kStreamWaves;
 
 // ------------------------------------------------------------------ token access
 
@@ -337,99 +338,90 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
 // ================================================================== 2. stream
 
 template <int R, int P, int SF>
-__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(R <= 2 ? 4 : 1))) void select_stream(SelectArgs a) {
+__global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
   constexpr int S = R * 16;
-  constexpr bool BF = SF == 3;              // BF16 keys
+  constexpr bool BF = SF == 3;                 // BF16 keys
   constexpr int RP = TokenPieces<R, BF>::value;
-  constexpr int HPW = 64 / P;               // KV heads covered by one wavefront
-  constexpr int PF = RP >= 16 ? 1 : 16 / RP;  // pages of a wavefront (all in flight at once)
-  constexpr int RL = 4 * PF * P + kRegionPad; // entries of one (chunk, KV head) region
-  __shared__ uint32_t wcnt[4][HPW];
-  __shared__ __align__(16) uint2 stage[HPW * 4 * PF * P];   // [head][wavefront][PF * P]
-  const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
-  const int hg = blockIdx.x, c = blockIdx.y, b = blockIdx.z;   // chunk c = 4 wavefronts
+  constexpr int PR = 64 / P;                   // pages of one round: lane = (page of the round, slot)
+  constexpr int NR = RP >= 16 ? 1 : 16 / RP;   // rounds (tokens per lane), all loads in flight together
+  constexpr int WP = NR * PR;                  // pages of a wavefront = one chunk
+  constexpr int RL = WP * P + kRegionPad;      // entries of one (chunk, KV head) region
+  __shared__ __align__(16) uint2 stage[kStreamWaves][WP * P];
+  const int lane = lane_id();
+  // wavefront -> (KV head of the block's head group, chunk of the block's
+  // chunk group); the index is made wave-uniform explicitly so that the head's
+  // projected query can live in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int hl = w % a.heads_pb, cw = w / a.heads_pb;
+  const int head = blockIdx.x * a.heads_pb + hl;
+  const int c = blockIdx.y * a.chunks_pb + cw;
+  const int b = blockIdx.z;
   const int N = seq_len_of(a, b);
   const int n_pages = (N + P - 1) / P;
-  if (c * a.cp >= n_pages) return;           // uniform over the block
-  const int page0 = c * a.cp + w * PF;
-  const bool any = page0 < n_pages;
-  const int hl = lane / P, slot = lane % P;
-  const int head = hg * HPW + hl;
-  const bool active = head < a.Hkv;
-  const int headc = active ? head : 0;
-  const int64_t bh = (int64_t)b * a.Hkv + headc;
+  if (cw >= a.chunks_pb || head >= a.Hkv || c * WP >= n_pages) return;   // uniform over the wavefront
+  const int64_t bh = (int64_t)b * a.Hkv + head;
+  const int pr = lane / P, slot = lane % P;
+  const int page0 = c * WP;
 
-  // physical pages of this wavefront: lane i < PF holds page page0 + i
+  // this chunk's physical pages: lane i < WP holds page page0 + i
   int phys_l = 0;
-  if (lane < PF && page0 + lane < n_pages) phys_l = a.block_table[(int64_t)b * a.max_pages + page0 + lane];
-  uint4 pc[PF][RP];
-  float sc[PF];
+  if (lane < WP && page0 + lane < n_pages) phys_l = a.block_table[(int64_t)b * a.max_pages + page0 + lane];
+  uint4 pc[NR][RP];
+  float sc[NR];
 #pragma unroll
-  for (int f = 0; f < PF; ++f) {
-    const int64_t phys = __builtin_amdgcn_readlane(phys_l, f);
-    if (active && page0 + f < n_pages) load_token_sf<RP, SF>(a, phys, head, slot, pc[f], sc[f]);
+  for (int k = 0; k < NR; ++k) {
+    const int pg = k * PR + pr;                // page of the chunk this lane reads in round k
+    const int64_t phys = __shfl(phys_l, pg);
+    if (page0 + pg < n_pages) load_token_sf<RP, SF>(a, phys, head, slot, pc[k], sc[k]);
   }
+  // the head's projected query, uniform over the wavefront
   float qh[S];
   {
     const float* src = a.qhat + bh * S;
 #pragma unroll
     for (int i = 0; i < S; i += 4) {
       const float4 v = *reinterpret_cast<const float4*>(src + i);
-      qh[i] = v.x;
-      qh[i + 1] = v.y;
-      qh[i + 2] = v.z;
-      qh[i + 3] = v.w;
+      qh[i] = uniform_f(v.x);
+      qh[i + 1] = uniform_f(v.y);
+      qh[i + 2] = uniform_f(v.z);
+      qh[i + 3] = uniform_f(v.w);
     }
   }
   uint32_t tau = a.tau[bh];
-  if (tau == 0u) tau = 1u;                   // key 0 marks "no token"
+  if (tau == 0u) tau = 1u;                     // key 0 marks "no token"
   const int64_t maxN = (int64_t)a.max_pages * P;
   float* sout = a.scores_out ? a.scores_out + bh * maxN : nullptr;
 
-  // each page's keys >= tau go, in position order, to this wavefront's part of
-  // the LDS staging area of its KV head (right after the ballot: no key or mask
-  // stays live across the block barrier)
-  const uint64_t hmask = (P == 64) ? ~0ull : (((1ull << (P & 63)) - 1ull) << (hl * P));
-  uint2* st = stage + (hl * 4 + w) * (PF * P);
+  // each round's keys >= tau go, in position order (round-major, then lane),
+  // to this wavefront's LDS staging area
+  uint2* st = stage[threadIdx.x >> 6];
   uint32_t cnt = 0;
 #pragma unroll
-  for (int f = 0; f < PF; ++f) {
-    const int t = (page0 + f) * P + slot;
+  for (int k = 0; k < NR; ++k) {
+    const int t = (page0 + k * PR + pr) * P + slot;
     uint32_t key = 0u;
-    if (any && active && t < N) {
-      const float s = score_token<R, BF>(pc[f], qh) * sc[f];
+    if (t < N) {
+      const float s = score_token<R, BF>(pc[k], qh) * sc[k];
       key = score_key(s);
       if (sout) sout[t] = s;
     }
-    const uint64_t m = ballot(key >= tau) & hmask;
+    const uint64_t m = ballot(key >= tau);
     if (m & (1ull << lane)) st[cnt + lanes_below(m)] = make_uint2(key, (uint32_t)t);
     cnt += (uint32_t)__popcll(m);
   }
-  if (slot == 0) wcnt[w][hl] = cnt;
-  __syncthreads();
-  // every region goes out as whole 128-byte lines: a header entry (x = the
-  // chunk's count), then the four wavefronts' candidates in wavefront order
-  // (= position order), the tail of the last line padded (scattered
-  // partial-line stores of the candidates measured 6.8 us slower at 128K)
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    const int hh = hg * HPW + h;
-    if (hh >= a.Hkv) break;                    // uniform
-    const uint32_t n0 = wcnt[0][h], n1 = wcnt[1][h], n2 = wcnt[2][h], n3 = wcnt[3][h];
-    const uint32_t o1 = n0, o2 = o1 + n1, o3 = o2 + n2, n = o3 + n3;
-    const int len = (int)((n + 16) & ~15u);    // header + n entries, whole lines
-    uint2* dst = a.cand + (((int64_t)b * a.Hkv + hh) * a.max_chunks + c) * RL;
-    const uint2* sh = stage + h * 4 * (PF * P);
-    for (int e = (int)threadIdx.x; e < len; e += kStreamThreads) {
-      const uint32_t k = (uint32_t)e - 1u;
-      uint2 v = make_uint2(n, 0u);
-      if (e > 0) {
-        const int wv = k >= o3 ? 3 : (k >= o2 ? 2 : (k >= o1 ? 1 : 0));
-        const uint32_t ov = wv == 3 ? o3 : (wv == 2 ? o2 : (wv == 1 ? o1 : 0u));
-        v = k < n ? sh[wv * (PF * P) + (k - ov)] : make_uint2(0u, 0u);
-      }
-      dst[e] = v;
-    }
+  // the staged entries were written by this wavefront's own LDS instructions,
+  // which complete in order; wait for them before reading them back
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // the region goes out as whole 128-byte lines: a header entry (x = the
+  // count), then the candidates, the last line padded (scattered partial-line
+  // stores of the candidates had measured 6.8 us slower at 128K)
+  const int len = (int)((cnt + 16) & ~15u);
+  uint2* dst = a.cand + (bh * a.max_chunks + c) * (int64_t)RL;
+  for (int e = lane; e < len; e += 64) {
+    const uint32_t k = (uint32_t)e - 1u;
+    uint2 v = make_uint2(cnt, 0u);
+    if (e > 0) v = k < cnt ? st[k] : make_uint2(0u, 0u);
+    dst[e] = v;
   }
 }
 
@@ -631,15 +623,15 @@ namespace {
 
 template <int R, int P, bool BF>
 hipError_t launch_select_rpb(const SelectArgs& a, int stages, hipStream_t s) {
-  constexpr int HPW = 64 / P;
   hipError_t e = hipSuccess;
   if (stages & 1) {
     hipLaunchKernelGGL((select_prologue<R, BF>), dim3(a.Hkv, a.batch), dim3(kPrologueThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2) {
-    const int hg = (a.Hkv + HPW - 1) / HPW;
-    const dim3 grid(hg, a.max_chunks, a.batch);
+    const int hgroups = (a.Hkv + a.heads_pb - 1) / a.heads_pb;
+    const int cgroups = (a.max_chunks + a.chunks_pb - 1) / a.chunks_pb;
+    const dim3 grid(hgroups, cgroups, a.batch);
     if (BF)
       hipLaunchKernelGGL((select_stream<R, P, 3>), grid, dim3(kStreamThreads), 0, s, a);
     else if (a.sfmt == 1)
