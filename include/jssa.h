@@ -214,6 +214,23 @@ int32_t jssa_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
                     const int32_t* indices, float sm_scale, uint16_t* out, float* lse_out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* jssa_attend_noalloc — jssa_attend for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results, with no workspace.  The
+ * split-K partials go to a device array inside the library, 64 MiB per GPU,
+ * which each GPU the library runs on holds until the process ends; the call
+ * itself allocates nothing.
+ * Returns JSSA_ERR_WORKSPACE when the shape's partials exceed that array
+ * (batch * Hq * splits * partials per split * (d_v + 2) floats; about 4 MiB at
+ * batch 8, 32 query heads, d = 128, 128K context), JSSA_ERR_HIP when the array
+ * cannot be located on the current device.  Every call on one GPU uses the
+ * same array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. */
+int32_t jssa_attend_noalloc(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* indices, float sm_scale, uint16_t* out, float* lse_out,
+                            hipStream_t stream);
+
 /* jssa_decode — one decode step: [jssa_store of k_new at slot_new, skipped when
  * k_new is NULL] -> jssa_select -> jssa_attend, all on `stream`.  k_new holds
  * one new key per sequence (T = batch), i.e. the token at position

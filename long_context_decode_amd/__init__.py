@@ -10,6 +10,6 @@ from ._lib import (  # noqa: F401
     JSSAError, Shape, make_shape, shape_for, status_string, workspace_bytes, decode_single_launch, kp_page_bytes,
     attend_splits,
     alloc_workspace,
-    alloc_scoring_cache, jssa_store, jssa_select, jssa_attend, jssa_decode, jssa_full_decode, jssa_gather_attend,
+    alloc_scoring_cache, jssa_store, jssa_select, jssa_attend, jssa_attend_noalloc, jssa_decode, jssa_full_decode, jssa_gather_attend,
     calib_workspace_bytes, jssa_calib_moments, jssa_basis, raw_library,
 )

@@ -30,7 +30,7 @@ EXPORTED = ("jssa_status_string", "jssa_workspace_bytes", "jssa_decode_path", "j
             "jssa_kp_page_bytes", "jssa_store",
             "jssa_select",
             "jssa_select_stages",
-            "jssa_attend", "jssa_decode", "jssa_full_decode", "jssa_gather_attend", "jssa_calib_workspace_bytes",
+            "jssa_attend", "jssa_attend_noalloc", "jssa_decode", "jssa_full_decode", "jssa_gather_attend", "jssa_calib_workspace_bytes",
             "jssa_calib_moments", "jssa_basis")
 
 
@@ -74,6 +74,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "jssa_select": (I32, [S, P, P, P, P, P, P, P, P, P, SZ, P]),
         "jssa_select_stages": (I32, [S, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
         "jssa_attend": (I32, [S, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]),
+        "jssa_attend_noalloc": (I32, [S, P, P, P, P, P, P, ctypes.c_float, P, P, P]),
         "jssa_decode": (I32, [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]),
         "jssa_full_decode": (I32, [S, P, P, P, P, P, I32, ctypes.c_float, P, P, P, SZ, P]),
         "jssa_gather_attend": (I32, [S, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P]),
@@ -276,6 +277,22 @@ def jssa_attend(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: O
             _ptr("lse_out", lse_out, torch.float32, (shape.batch, shape.num_q_heads), optional=True),
             *_ws(shape, workspace))
     _check("jssa_attend", _lib.jssa_attend(ctypes.byref(shape), *args, _stream()))
+
+
+def jssa_attend_noalloc(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
+                        block_table: torch.Tensor, seq_lens: torch.Tensor, indices: torch.Tensor, sm_scale: float,
+                        out: torch.Tensor, lse_out: Optional[torch.Tensor] = None) -> None:
+    """jssa_attend without a workspace (the library's own per-GPU scratch array holds the partials)."""
+    n, cs = _cache_shape(shape, k_cache)
+    args = (_ptr("q", q, torch.bfloat16, (shape.batch, shape.num_q_heads, shape.head_dim)),
+            _ptr("k_cache", k_cache, torch.bfloat16, cs),
+            _ptr("v_cache", v_cache, torch.bfloat16, cs, optional=shape.kind == KIND_MLA),
+            *_table_args(shape, block_table, seq_lens),
+            _ptr("indices", indices, torch.int32, (shape.batch, shape.num_kv_heads, shape.budget)),
+            ctypes.c_float(sm_scale),
+            _ptr("out", out, torch.bfloat16, (shape.batch, shape.num_q_heads, shape.v_dim)),
+            _ptr("lse_out", lse_out, torch.float32, (shape.batch, shape.num_q_heads), optional=True))
+    _check("jssa_attend_noalloc", _lib.jssa_attend_noalloc(ctypes.byref(shape), *args, _stream()))
 
 
 def jssa_decode(shape: Shape, q: torch.Tensor, k_new: Optional[torch.Tensor], slot_new: Optional[torch.Tensor],

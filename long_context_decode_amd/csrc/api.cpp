@@ -270,12 +270,12 @@ void attend_plan(const Plan& p, bool sparse, int window, int* splits, int* len) 
   }
 }
 
-int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
-                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, int window,
-                  float sm_scale, uint16_t* out, float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !out || !ws) return JSSA_ERR_NULL;
-  if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
-  if (window < 0) return JSSA_ERR_SHAPE;
+// The attention launches with the split-K partials at part_o / part_ml
+// (pointer checks done by the caller).
+int32_t run_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, int window,
+                   float sm_scale, uint16_t* out, float* lse_out, float* part_o, float* part_ml,
+                   hipStream_t stream) {
   AttendArgs a{};
   a.q = q;
   a.k_cache = k_cache;
@@ -283,8 +283,8 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.indices = indices;
-  a.part_o = at<float>(ws, p.off_part_o);
-  a.part_ml = at<float>(ws, p.off_part_ml);
+  a.part_o = part_o;
+  a.part_ml = part_ml;
   a.out = out;
   a.lse_out = lse_out;
   a.sm_log2 = sm_scale * kLog2e;
@@ -301,6 +301,16 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
   if (a.splits > p.split_cap) return JSSA_ERR_UNSUPPORTED;    // cannot happen (split_capacity)
   if (p.mla) return hip_status(launch_mla_attend(a, stream));
   return hip_status(launch_attend(a, p.d, stream));
+}
+
+int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, int window,
+                  float sm_scale, uint16_t* out, float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !out || !ws) return JSSA_ERR_NULL;
+  if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
+  if (window < 0) return JSSA_ERR_SHAPE;
+  return run_attend(p, q, k_cache, v_cache, block_table, seq_lens, indices, window, sm_scale, out, lse_out,
+                    at<float>(ws, p.off_part_o), at<float>(ws, p.off_part_ml), stream);
 }
 
 }  // namespace
@@ -404,6 +414,27 @@ int32_t jssa_attend(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
   if (!indices) return JSSA_ERR_NULL;
   return do_attend(p, q, k_cache, v_cache, block_table, seq_lens, indices, 0, sm_scale, out, lse_out, workspace,
                    workspace_bytes, stream);
+}
+
+int32_t jssa_attend_noalloc(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* indices, float sm_scale, uint16_t* out, float* lse_out,
+                            hipStream_t stream) {
+  Plan p;
+  const int32_t st = make_plan(shape, &p);
+  if (st != JSSA_OK) return st;
+  if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !indices || !out) return JSSA_ERR_NULL;
+  // the partials of this call's split plan, laid out from the start of the
+  // library's scratch array: o [batch, Hq, splits * parts, dv], then (m, l)
+  int splits = 0, len = 0;
+  attend_plan(p, true, 0, &splits, &len);
+  const size_t parts = (size_t)p.batch * p.Hq * splits * (p.mla ? 1 : 4);
+  const size_t o_bytes = align_up(parts * p.dv * sizeof(float));
+  if (o_bytes + align_up(parts * 2 * sizeof(float)) > kAttendScratchBytes) return JSSA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (attend_scratch(&scratch) != hipSuccess) return JSSA_ERR_HIP;
+  return run_attend(p, q, k_cache, v_cache, block_table, seq_lens, indices, 0, sm_scale, out, lse_out,
+                    static_cast<float*>(scratch), at<float>(scratch, o_bytes), stream);
 }
 
 int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* k_new, const int32_t* slot_new,

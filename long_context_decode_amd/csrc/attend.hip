@@ -13,11 +13,38 @@
 // wavefront writes its own partial (o, m, l), and merge_kernel combines them.
 // DENSE instantiates the full-KV / sliding-window baseline (positions [lo, N)
 // instead of an index list).
+#include <mutex>
+
 #include "attend_core.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace jssa {
+
+// Split-K partials of jssa_attend_noalloc (for callers that cannot allocate):
+// each GPU the library runs on holds its own copy until the process ends.  In
+// host code this name is only a stand-in for the symbol; the device address
+// comes from hipGetSymbolAddress (attend_scratch).
+static __device__ __align__(256) unsigned char scratch[kAttendScratchBytes];
+
+hipError_t attend_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device dev current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -119,6 +119,10 @@ hipError_t launch_select(const SelectArgs& a, int stages, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_mla_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttendArgs& a, int dv, hipStream_t s);
+// the partials scratch of jssa_attend_noalloc: a file-scope device array of
+// kAttendScratchBytes, one per GPU; *ptr = its address on the current device
+constexpr size_t kAttendScratchBytes = (size_t)64 << 20;
+hipError_t attend_scratch(void** ptr);
 hipError_t launch_calib(const CalibArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);

@@ -224,3 +224,24 @@ def test_attend_splits_known_shapes():
     assert L.attend_splits(sh, False, 4096) == (16, 16)
     with pytest.raises(L.JSSAError):
         L.attend_splits(sh, False, -1)
+
+
+def test_noalloc_attend_refuses_oversized_and_null_before_any_launch():
+    """jssa_attend_noalloc checks pointers, then the partials' size against its 64 MiB scratch array, before it
+    touches a device (status codes only; the pointers are never dereferenced)."""
+    lib = L.raw_library()
+    fake = ctypes.c_void_p(16)
+    # 256 sequences x 64 query heads x d 256: the partials exceed the scratch array
+    big = _shape(batch=256, num_q_heads=64, num_kv_heads=8, head_dim=256, max_pages_per_seq=1024, budget=4096)
+    splits, _ = L.attend_splits(big, True)
+    assert 256 * 64 * splits * 4 * (256 + 2) * 4 > 64 << 20
+    st = lib.jssa_attend_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, ctypes.c_float(0.1), fake,
+                                 None, None)
+    assert st == -4                                           # JSSA_ERR_WORKSPACE
+    small = _shape()
+    st = lib.jssa_attend_noalloc(ctypes.byref(small), None, fake, fake, fake, fake, fake, ctypes.c_float(0.1), fake,
+                                 None, None)
+    assert st == -1                                           # JSSA_ERR_NULL
+    st = lib.jssa_attend_noalloc(ctypes.byref(_shape(budget=0)), fake, fake, fake, fake, fake, fake,
+                                 ctypes.c_float(0.1), fake, None, None)
+    assert st == -2                                           # JSSA_ERR_SHAPE
