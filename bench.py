@@ -22,9 +22,10 @@ Prints one JSON line.
 Two helper modes turn rocprofv3 output into the short summaries kept under
 profiles/:
   --summarize-trace DIR   kernel-trace statistics -> markdown table
-  --summarize-counters FETCH_DIR WRITE_DIR   FETCH_SIZE / WRITE_SIZE per
-      dispatch of the score-stream kernel, scaled by the same counters on the
-      1 GiB elementwise probe (--copy-probe) -> JSON read back by this script
+  --summarize-counters READ_DIR WRITE_DIR SQ_DIR   three counter passes
+      (HBM reads, HBM writes, SQ busy/LDS counters) per dispatch of each hot
+      kernel, scaled by the same counters on the 1 GiB elementwise probe
+      (--copy-probe) -> JSON read back by this script, plus a markdown table
 """
 from __future__ import annotations
 
@@ -41,6 +42,21 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+
+def _early_cpu_threads(argv):
+    """--cpu-threads N has to reach the OpenBLAS and OpenMP pools before numpy and torch load them: a limit set
+    later is not honoured by every pool on every host."""
+    for i, a in enumerate(argv):
+        v = a.split("=", 1)[1] if a.startswith("--cpu-threads=") else (
+            argv[i + 1] if a == "--cpu-threads" and i + 1 < len(argv) else None)
+        if v is not None and v.isdigit() and int(v) > 0:
+            for name in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+                os.environ[name] = v
+
+
+if __name__ == "__main__":
+    _early_cpu_threads(sys.argv[1:])
+
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 STREAM_KERNEL = "select_stream"
@@ -51,7 +67,7 @@ METRIC = "decode attn-stage steps/s @128K; HBM GB/s vs peak; speedup vs full-KV 
 
 
 def counters_path(workload):
-    return os.path.join(ROOT, "profiles", f"counters_select_stream_{workload}.json")
+    return os.path.join(ROOT, "profiles", f"counters_{workload}.json")
 
 
 def _code_lines(text: str):
@@ -278,6 +294,34 @@ def time_stages(stage_fns, steps, n_rep):
     return res
 
 
+def time_stages_graph(stage_fns, n_rep, launches=60, replays=4):
+    """Average duration of each stage on the GPU: `launches` launches of that stage alone (rotating over
+    n_rep units) captured in one HIP graph, replayed `replays` times between two HIP events on the current
+    stream (the graph runs on it).  No host launch interval enters, so short kernels are timed too; the
+    figure includes the gap between consecutive kernels of a graph."""
+    import torch
+    res = {}
+    for name, fn in stage_fns.items():
+        for i in range(2):
+            fn(i % n_rep)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(launches):
+                fn(i % n_rep)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / (launches * replays)
+        del g
+    return res
+
+
 # ----------------------------------------------------------------------------- CPU oracle
 
 def _host_threads():
@@ -358,7 +402,8 @@ def traffic_for(workload):
     c = json.load(open(path))
     if c.get("source_hash") != _src_hash(*STREAM_SOURCES):
         return None
-    return c.get("hbm_bytes_per_dispatch")
+    k = c.get("kernels", {}).get(STREAM_KERNEL)
+    return None if k is None else k.get("hbm_bytes_per_dispatch")
 
 
 def _rows(d, suffix):
@@ -372,36 +417,128 @@ def _rows(d, suffix):
     return out
 
 
-def _counter_per_dispatch(d, counter, match):
-    """Mean over the dispatches of kernels whose name contains `match` of one counter (summed over its
-    instances within a dispatch)."""
-    per = {}
+# rocprofv3 counter passes (one run each; at most 4 TCC, 8 SQ and 2 GRBM counters per pass)
+COUNTER_PASSES = {
+    "read": ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum"],
+    "write": ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_HIT_sum", "TCC_MISS_sum"],
+    "sq": ["SQ_WAVES", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES",
+           "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"],
+}
+HOT_KERNELS = ("store_kernel", "select_prologue", "select_stream", "select_finish", "attend_kernel", "merge_kernel",
+               "mla_sparse_kernel", "mla_dense_kernel", "decode_fused_kernel", "gather_kernel", PROBE_KERNEL)
+CU_NUM, SIMD_NUM = 256, 1024
+
+
+def _kernel_group(name):
+    """The library kernel (or the probe) a dispatch belongs to; the sparse and dense GQA attention and the
+    merge of each are told apart by their template arguments."""
+    for k in HOT_KERNELS:
+        if k in name:
+            if k == "attend_kernel":
+                return "attend_kernel (dense)" if re.search(r"attend_kernel<\d+, \d+, true>|Lb1E", name) else \
+                    "attend_kernel (sparse)"
+            return k
+    return None
+
+
+# counters whose instances (one per XCD) are combined with max, as the rocprofv3 derived metrics do; the
+# others are summed over their instances
+MAX_OVER_INSTANCES = ("GRBM_GUI_ACTIVE",)
+
+
+def _per_dispatch(d):
+    """{kernel group: {counter: mean over the group's dispatches of the counter within a dispatch (summed over
+    its instances, or their max for MAX_OVER_INSTANCES)}}."""
+    acc = {}
     for r in _rows(d, "counter_collection.csv"):
-        if r.get("Counter_Name") != counter or match not in r.get("Kernel_Name", ""):
+        g = _kernel_group(r.get("Kernel_Name", ""))
+        if g is None:
             continue
-        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r.get("Kernel_Name"))
-        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-    if not per:
-        raise SystemExit(f"{counter}: no dispatch of a kernel matching {match!r} in {d}")
-    return sum(per.values()) / len(per), len(per)
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        name, v = r["Counter_Name"], float(r["Counter_Value"])
+        per = acc.setdefault(g, {}).setdefault(name, {})
+        if name in MAX_OVER_INSTANCES:
+            per[key] = max(per.get(key, v), v)
+        else:
+            per[key] = per.get(key, 0.0) + v
+    out = {}
+    for g, cs in acc.items():
+        out[g] = {c: sum(v.values()) / len(v) for c, v in cs.items()}
+        out[g]["dispatches"] = max(len(v) for v in cs.values())
+    return out
 
 
-def summarize_counters(fetch_dir, write_dir, workload, score_bytes, command):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the stream kernel, each scaled by the ratio of the probe's
-    known bytes to what the same counter reads for it."""
-    f_st, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", STREAM_KERNEL)
-    w_st, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", STREAM_KERNEL)
-    f_pr, _ = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", PROBE_KERNEL)
-    w_pr, _ = _counter_per_dispatch(write_dir, "WRITE_SIZE", PROBE_KERNEL)
-    kf = PROBE_BYTES / (f_pr * 1024.0)
-    kw = PROBE_BYTES / (w_pr * 1024.0)
-    hbm = f_st * 1024.0 * kf + w_st * 1024.0 * kw
-    return {"kernel": "select_stream", "workload": workload, "source_hash": _src_hash(*STREAM_SOURCES),
-            "fetch_kib_per_dispatch": round(f_st, 1), "write_kib_per_dispatch": round(w_st, 1),
-            "dispatches": [nf, nw], "probe_fetch_kib": round(f_pr, 1), "probe_write_kib": round(w_pr, 1),
-            "scale_fetch": round(kf, 4), "scale_write": round(kw, 4),
-            "hbm_bytes_per_dispatch": int(hbm), "algorithmic_bytes_per_dispatch": int(score_bytes),
-            "traffic_over_algorithmic": round(hbm / score_bytes, 4), "command": command}
+def summarize_counters(read_dir, write_dir, sq_dir, workload, alg_bytes, command):
+    """Per hot kernel and dispatch: HBM bytes read and written, L2 hit rate, VALU busy, MFMA busy and LDS
+    bank-conflict time, from the three counter passes.  Bytes read: the L2's 32-byte requests count 32 B and
+    its other read requests the size that makes the probe's known read (1 GiB) come out, derived from the
+    probe's own counters; bytes written: the WRITE_SIZE definition (32- and 64-byte requests), checked on the
+    probe's 1 GiB write."""
+    rd, wr, sq = _per_dispatch(read_dir), _per_dispatch(write_dir), _per_dispatch(sq_dir)
+    pr, pw = rd[PROBE_KERNEL], wr[PROBE_KERNEL]
+    full = pr["TCC_EA0_RDREQ_sum"] - pr["TCC_EA0_RDREQ_32B_sum"]
+    bytes_per_req = (PROBE_BYTES - 32.0 * pr["TCC_EA0_RDREQ_32B_sum"]) / full
+    fetch_def = (pr["TCC_BUBBLE_sum"] * 128 + (pr["TCC_EA0_RDREQ_sum"] - pr["TCC_BUBBLE_sum"] -
+                                                pr["TCC_EA0_RDREQ_32B_sum"]) * 64 + pr["TCC_EA0_RDREQ_32B_sum"] * 32)
+
+    def wbytes(c):
+        return (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"]) * 32 + c["TCC_EA0_WRREQ_64B_sum"] * 64
+
+    kernels = {}
+    for g in sorted(set(rd) | set(wr) | set(sq)):
+        k = {}
+        if g in rd:
+            c = rd[g]
+            k["read_bytes"] = int(32 * c["TCC_EA0_RDREQ_32B_sum"] +
+                                  bytes_per_req * (c["TCC_EA0_RDREQ_sum"] - c["TCC_EA0_RDREQ_32B_sum"]))
+            k["read_requests"] = int(c["TCC_EA0_RDREQ_sum"])
+            k["read_128b_bubble"] = int(c["TCC_BUBBLE_sum"])
+        if g in wr:
+            c = wr[g]
+            k["write_bytes"] = int(wbytes(c))
+            hm = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
+            k["l2_hit_rate"] = round(c["TCC_HIT_sum"] / hm, 4) if hm else None
+        if "read_bytes" in k and "write_bytes" in k:
+            k["hbm_bytes_per_dispatch"] = k["read_bytes"] + k["write_bytes"]
+        if g in sq:
+            c = sq[g]
+            gui = c["GRBM_GUI_ACTIVE"]
+            k["gui_active_cycles"] = int(gui)
+            k["valu_busy_pct"] = round(100.0 * c["SQ_ACTIVE_INST_VALU"] / CU_NUM / gui, 2) if gui else None
+            k["mfma_busy_pct"] = round(100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM), 2) if gui else None
+            k["lds_bank_conflict_pct"] = round(100.0 * c["SQ_LDS_BANK_CONFLICT"] / gui / CU_NUM, 3) if gui else None
+            k["lds_instructions"] = int(c["SQ_INSTS_LDS"])
+            k["waves"] = int(c["SQ_WAVES"])
+        k["dispatches"] = max(x[g]["dispatches"] for x in (rd, wr, sq) if g in x)
+        if g in alg_bytes:
+            k["algorithmic_bytes_per_dispatch"] = alg_bytes[g]
+            if "hbm_bytes_per_dispatch" in k:
+                k["traffic_over_algorithmic"] = round(k["hbm_bytes_per_dispatch"] / alg_bytes[g], 4)
+        kernels[g] = k
+    return {"workload": workload, "source_hash": _src_hash(*STREAM_SOURCES),
+            "probe": {"kernel": PROBE_KERNEL, "bytes_read": PROBE_BYTES, "bytes_written": PROBE_BYTES,
+                      "read_requests": int(pr["TCC_EA0_RDREQ_sum"]), "read_32b": int(pr["TCC_EA0_RDREQ_32B_sum"]),
+                      "read_128b_bubble": int(pr["TCC_BUBBLE_sum"]),
+                      "bytes_per_read_request": round(bytes_per_req, 2),
+                      "fetch_size_definition_bytes": int(fetch_def),
+                      "write_size_definition_bytes": int(wbytes(pw))},
+            "kernels": kernels, "command": command}
+
+
+def counters_markdown(c):
+    lines = [f"# rocprofv3 counters, {c['workload']}", "", f"Command: `{c['command']}`", "",
+             f"Probe (torch neg over 1 GiB): {c['probe']['read_requests']} L2 read requests for 2^30 bytes = "
+             f"{c['probe']['bytes_per_read_request']} bytes per request ({c['probe']['read_128b_bubble']} counted "
+             f"as 128-byte); the FETCH_SIZE definition gives {c['probe']['fetch_size_definition_bytes']} bytes. "
+             f"WRITE_SIZE definition: {c['probe']['write_size_definition_bytes']} bytes for the 2^30 written.", "",
+             "| kernel | dispatches | HBM read MB | HBM write MB | traffic / algorithmic | L2 hit | VALU busy % | "
+             "MFMA busy % | LDS bank conflict % |", "|---|---|---|---|---|---|---|---|---|"]
+    for g, k in c["kernels"].items():
+        f = lambda x, d=1: "" if x is None else (f"{x / 1e6:.{d}f}" if isinstance(x, int) else f"{x}")  # noqa: E731
+        lines.append(f"| `{g}` | {k.get('dispatches')} | {f(k.get('read_bytes'), 2)} | {f(k.get('write_bytes'), 2)} | "
+                     f"{k.get('traffic_over_algorithmic', '')} | {k.get('l2_hit_rate', '')} | "
+                     f"{k.get('valu_busy_pct', '')} | {k.get('mfma_busy_pct', '')} | {k.get('lds_bank_conflict_pct', '')} |")
+    return "\n".join(lines) + "\n"
 
 
 def summarize_trace(d, command):
@@ -518,7 +655,11 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated per step (0: automatic)")
     ap.add_argument("--cpu-seqs", type=int, default=-1,
                     help="sequences per CPU-oracle pass (0: skip; default the whole batch on the default workload)")
-    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU oracle's BLAS/OpenMP pools (0: all the host offers)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="no HIP graphs at all: skip the graph timing of the step and time each stage from "
+                         "host-launched calls (for counter collection)")
     ap.add_argument("--scale-format", default="fp32", choices=["fp32", "e8m0", "none", "bf16"],
                     help="scoring-cache format: FP8 with an fp32 scale per token (default), with a one-byte power of two, "
                          "with no scale, or BF16 projected keys")
@@ -530,7 +671,8 @@ def main():
                     help="top-B recall vs rank for the joint, key-only and random bases (prints one JSON line)")
     ap.add_argument("--ranks", default="4,8,16,32,48,64")
     ap.add_argument("--summarize-trace", metavar="DIR")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("READ_DIR", "WRITE_DIR", "SQ_DIR"),
+                    help="rocprofv3 counter passes (COUNTER_PASSES) -> profiles/counters_<workload>.json / .md")
     ap.add_argument("--command", default="", help="profiling command recorded in a summary")
     ap.add_argument("--out", help="summary output file")
     args = ap.parse_args()
@@ -538,17 +680,24 @@ def main():
     if args.summarize_trace or args.summarize_counters:
         if args.summarize_trace:
             txt = summarize_trace(args.summarize_trace, args.command)
-        else:
-            from synth import WORKLOADS
-            w = WORKLOADS[args.workload]
-            score = layer_bytes(w, [w.seq_len] * w.batch, "sparse")["score"]
-            txt = json.dumps(summarize_counters(*args.summarize_counters, args.workload, score, args.command),
-                             indent=1) + "\n"
-        if args.out:
-            with open(args.out, "w") as f:
-                f.write(txt)
-        else:
-            print(txt)
+            if args.out:
+                with open(args.out, "w") as f:
+                    f.write(txt)
+            else:
+                print(txt)
+            return
+        from synth import WORKLOADS
+        w = WORKLOADS[args.workload]
+        lb = layer_bytes(w, [w.seq_len] * w.batch, "sparse")
+        alg = {STREAM_KERNEL: lb["score"],
+               "attend_kernel (sparse)": lb["selected_kv"] + lb["indices"] // 2,
+               "mla_sparse_kernel": lb["selected_kv"] + lb["indices"] // 2}
+        c = summarize_counters(*args.summarize_counters, args.workload, alg, args.command)
+        with open(counters_path(args.workload), "w") as f:
+            f.write(json.dumps(c, indent=1) + "\n")
+        with open(counters_path(args.workload)[:-5] + ".md", "w") as f:
+            f.write(counters_markdown(c))
+        print(counters_markdown(c))
         return
 
     if args.recall_sweep:
@@ -656,7 +805,7 @@ def main():
     for i in range(3):
         for f in stages.values():
             f(i)
-    stage_ms = time_stages(stages, args.steps, n_units)
+    stage_ms = time_stages(stages, args.steps, n_units) if args.no_graph else time_stages_graph(stages, n_units)
 
     # achievable-bandwidth probe: torch's elementwise negation over 1 GiB (1 GiB read + 1 GiB written);
     # with --copy-probe it runs once more alone, as the reference dispatch for counter scaling
@@ -672,11 +821,17 @@ def main():
     lb = layer_bytes(w, seq, "sparse", args.scale_format)
     stream_bytes = lb["score"]
     achieved = stream_bytes / (stage_ms["select_stream"] * 1e-3) / 1e9
+    # the dominant kernel alone (the score stream); the whole step's figure is step_roofline
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_for(w.name) if args.scale_format == "fp32" else None,
-                "kernel": "select_stream (FP8 score stream + candidate compaction)",
+                "kernel": "select_stream (FP8 score stream + candidate compaction; dominant kernel only)",
                 "bytes_per_launch": stream_bytes, "avg_launch_ms": round(stage_ms["select_stream"], 5)}
+    step_gbps = total_bytes / (ms * 1e-3) / 1e9
+    step_roofline = {"bound": "hbm", "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(step_gbps / HBM_PEAK_GBPS, 4), "bytes_per_step": total_bytes,
+                     "ms_per_step": round(ms, 5),
+                     "what": "whole step: store + select (prologue, stream, finish) + attend + merge, all layers"}
 
     extra = {}
     if w.kind == "mla":
@@ -691,7 +846,14 @@ def main():
 
     n_cpu = args.cpu_seqs if args.cpu_seqs >= 0 else (w.batch if w.name == "llama8b_128k" and
                                                        args.scale_format == "fp32" else 0)
-    cpu = cpu_baseline(w, case, min(n_cpu, w.batch)) if n_cpu > 0 and not w.window else None
+    cpu = None
+    if n_cpu > 0 and not w.window:
+        if args.cpu_threads > 0:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=args.cpu_threads):
+                cpu = cpu_baseline(w, case, min(n_cpu, w.batch))
+        else:
+            cpu = cpu_baseline(w, case, min(n_cpu, w.batch))
 
     cfg = {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
            "head_dim": w.head_dim, "seq_len": w.seq_len, "page_size": w.page_size, "rank": w.rank,
@@ -717,6 +879,7 @@ def main():
         "data": "synthetic (seeded anisotropic keys/queries, 1% planted needles, random page permutation)",
         "config": cfg,
         "roofline": roofline,
+        "step_roofline": step_roofline,
         "cpu_baseline": cpu,
         "hbm_gbps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),

@@ -37,23 +37,43 @@ def _write(path, header, rows):
         wr.writerows(rows)
 
 
-def test_counter_summary_scales_by_probe(tmp_path):
+def test_counter_summary_derives_request_size_from_probe(tmp_path):
+    """Three passes: the probe's 1 GiB read fixes the bytes of a full L2 read request (here 128, with none
+    counted as 128-byte 'bubbles': the FETCH_SIZE definition would count them as 64); 32-byte requests count
+    32; writes follow the WRITE_SIZE definition; busy and conflict percentages follow the rocprofv3
+    definitions (256 CUs, 1024 SIMDs)."""
     hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
-    fetch, write = tmp_path / "f", tmp_path / "w"
-    # the probe reads 1 GiB but the counter reports 0.5 GiB: factor 2
-    _write(str(fetch / "host" / "1_counter_collection.csv"), hdr, [
-        [1, "void jssa::select_stream<2, 16>(jssa::SelectArgs)", "FETCH_SIZE", 1000.0],
-        [1, "void jssa::select_stream<2, 16>(jssa::SelectArgs)", "FETCH_SIZE", 500.0],
-        [2, "void jssa::select_stream<2, 16>(jssa::SelectArgs)", "FETCH_SIZE", 1500.0],
-        [3, "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>", "FETCH_SIZE", 512.0 * 1024]])
-    _write(str(write / "host" / "1_counter_collection.csv"), hdr, [
-        [1, "void jssa::select_stream<2, 16>(jssa::SelectArgs)", "WRITE_SIZE", 100.0],
-        [3, "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>", "WRITE_SIZE", 1024.0 * 1024]])
-    r = bench.summarize_counters(str(fetch), str(write), "llama8b_128k", 10_000, "cmd")
-    assert r["fetch_kib_per_dispatch"] == 1500.0 and r["write_kib_per_dispatch"] == 100.0
-    assert r["scale_fetch"] == 2.0 and r["scale_write"] == 1.0
-    assert r["hbm_bytes_per_dispatch"] == int(1500 * 1024 * 2 + 100 * 1024)
+    st = "void jssa::select_stream<2, 16, 0>(jssa::SelectArgs)"
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>"
+    rd, wr, sq = tmp_path / "r", tmp_path / "w", tmp_path / "s"
+    _write(str(rd / "h" / "1_counter_collection.csv"), hdr, [
+        [1, st, "TCC_EA0_RDREQ_sum", 600.0], [1, st, "TCC_EA0_RDREQ_sum", 400.0],      # two instances, one dispatch
+        [1, st, "TCC_EA0_RDREQ_32B_sum", 10.0], [1, st, "TCC_BUBBLE_sum", 0.0],
+        [2, st, "TCC_EA0_RDREQ_sum", 1000.0], [2, st, "TCC_EA0_RDREQ_32B_sum", 10.0], [2, st, "TCC_BUBBLE_sum", 0.0],
+        [3, neg, "TCC_EA0_RDREQ_sum", float(2 ** 30 // 128)], [3, neg, "TCC_EA0_RDREQ_32B_sum", 0.0],
+        [3, neg, "TCC_BUBBLE_sum", 0.0]])
+    _write(str(wr / "h" / "1_counter_collection.csv"), hdr, [
+        [1, st, "TCC_EA0_WRREQ_sum", 100.0], [1, st, "TCC_EA0_WRREQ_64B_sum", 50.0],
+        [1, st, "TCC_HIT_sum", 30.0], [1, st, "TCC_MISS_sum", 70.0],
+        [3, neg, "TCC_EA0_WRREQ_sum", float(2 ** 30 // 64)], [3, neg, "TCC_EA0_WRREQ_64B_sum", float(2 ** 30 // 64)],
+        [3, neg, "TCC_HIT_sum", 0.0], [3, neg, "TCC_MISS_sum", 1.0]])
+    _write(str(sq / "h" / "1_counter_collection.csv"), hdr, [
+        [1, st, "GRBM_GUI_ACTIVE", 1000.0], [1, st, "GRBM_GUI_ACTIVE", 990.0],   # per-XCD instances: max
+        [1, st, "SQ_ACTIVE_INST_VALU", 64000.0],
+        [1, st, "SQ_VALU_MFMA_BUSY_CYCLES", 0.0], [1, st, "SQ_LDS_BANK_CONFLICT", 2560.0],
+        [1, st, "SQ_INSTS_LDS", 5.0], [1, st, "SQ_WAVES", 7.0], [1, st, "SQ_BUSY_CU_CYCLES", 1.0]])
+    r = bench.summarize_counters(str(rd), str(wr), str(sq), "llama8b_128k", {"select_stream": 254_080}, "cmd")
+    assert r["probe"]["bytes_per_read_request"] == 128.0
+    assert r["probe"]["fetch_size_definition_bytes"] == 2 ** 30 // 2
+    assert r["probe"]["write_size_definition_bytes"] == 2 ** 30
+    k = r["kernels"]["select_stream"]
+    assert k["read_bytes"] == 10 * 32 + 990 * 128 and k["write_bytes"] == 50 * 32 + 50 * 64
+    assert k["hbm_bytes_per_dispatch"] == k["read_bytes"] + k["write_bytes"]
+    assert k["l2_hit_rate"] == 0.3 and k["dispatches"] == 2
+    assert k["valu_busy_pct"] == 25.0 and k["mfma_busy_pct"] == 0.0 and k["lds_bank_conflict_pct"] == 1.0
+    assert k["traffic_over_algorithmic"] == round((k["read_bytes"] + k["write_bytes"]) / 254_080, 4)
     json.dumps(r)
+    assert "select_stream" in bench.counters_markdown(r)
 
 
 def test_trace_summary(tmp_path):
