@@ -189,12 +189,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   // the tile's 32 x 72 16-byte pieces, 9 per thread, all loads in flight
   // together.  A missing row (past the split's end) is loaded from the tile's
-  // first row, which always exists: its logits are masked to -inf, so its
-  // weight is 0 and its (finite) values add nothing.  `vld` records whether
-  // this lane's S row 16 rt + c of the tile exists.
+  // first row, which exists unless the index list holds a position outside
+  // [0, N) there (then row 0 of the cache, which exists whenever any row
+  // does): its logits are masked to -inf, so its weight is 0 and its
+  // (finite) values add nothing.  `vld` records whether this lane's S row
+  // 16 rt + c of the tile exists.
   auto fetch = [&](int kt, u32x4 (&reg)[kPieces], bool& vld) {
     const int* rw = rows + (kt % kTilesPerChunk) * kTile;
-    const int r0 = rw[0];
+    const int r0 = max(rw[0], 0);
     int rr[kPieces];
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) rr[k] = rw[(tid + k * kThreads) / (kD / 8)];

@@ -844,3 +844,71 @@ def test_nan_in_unused_slot_zero_does_not_reach_the_output():
     for window in (0, 100):
         L.jssa_full_decode(shape, qd, ld, None, btd, sld, window, w.sm_scale, out, ws)
         check_mla(lambda b: ogqa.window_indices(int(case.seq_lens[b]), window))
+
+
+def _spoil(idx, n, marks):
+    """Overwrite entries of an index list with positions outside [0, n): the attend kernels must skip them."""
+    bad = idx.copy()
+    for i, kind in marks:
+        bad[i] = {"neg": -1, "end": n, "far": n + 12345, "huge": 2 ** 30}[kind]
+    return bad
+
+
+def test_listed_positions_outside_the_sequence_are_skipped():
+    """Entries outside [0, N) of an index list (negative, N and beyond) are skipped wherever they fall: at the
+    first row of a tile or batch, and as a whole split of the MLA kernel, whose rows are then all missing.
+    The result is attention over the valid entries."""
+    w, case, m32, rows_k, rows_v, stored = _gqa("mid_sampled")
+    lay = case.layers[0]
+    q = bf16_bits(lay.q)
+    sl = case.seq_lens.numpy()
+    idx = np.full((w.batch, w.num_kv_heads, w.budget), -1, np.int32)
+    for b in range(w.batch):
+        qhat = ogqa.project_query(q[b], m32, w.group)
+        for h in range(w.num_kv_heads):
+            s = ogqa.scores(qhat[h], stored[b][0][:, h], stored[b][1][:, h])
+            sel, _ = ogqa.select_topb(s, w.budget)
+            idx[b, h] = _spoil(sel, int(sl[b]), [(0, "neg"), (64, "end"), (65, "far"), (128, "huge"),
+                                                 (255, "neg")] + [(i, "neg") for i in range(256, 320)])
+    shape = L.shape_for(w)
+    ws = L.alloc_workspace(shape)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    args = (shape, lay.q.to(DEV), lay.k_cache.to(DEV), lay.v_cache.to(DEV), case.block_table.to(DEV),
+            case.seq_lens.to(DEV), torch.from_numpy(idx).to(DEV), w.sm_scale, out, ws)
+    for fn in (L.jssa_attend, L.jssa_gather_attend):
+        fn(*args)
+        got = out.float().cpu().numpy()
+        assert np.isfinite(got).all()
+        for b in range(w.batch):
+            for h in range(w.num_kv_heads):
+                j0 = h * w.group
+                ok = idx[b, h][(idx[b, h] >= 0) & (idx[b, h] < int(sl[b]))]
+                o, _ = ogqa.attend_group(q[b, j0:j0 + w.group], rows_k[b][:, h], rows_v[b][:, h], ok, w.sm_scale)
+                check_attention(got[b, j0:j0 + w.group], o)
+
+    for name in ("mla_sampled", "mla_max_budget"):
+        w, case, m32, rows, stored = _mla(name)
+        q = bf16_bits(case.q)
+        sl = case.seq_lens.numpy()
+        shape = L.shape_for(w)
+        splits, _ = L.attend_splits(shape, True)
+        span = -(-min(w.budget, int(sl.max())) // splits)      # rows per split, about
+        idx = np.full((w.batch, 1, w.budget), -1, np.int32)
+        for b in range(w.batch):
+            s = ogqa.scores(omla.project_query(q[b], m32), stored[b][0], stored[b][1])
+            sel, _ = ogqa.select_topb(s, w.budget)
+            marks = [(0, "neg"), (32, "end"), (33, "far"), (96, "huge")]
+            marks += [(i, "neg") for i in range(2 * span, min(4 * span, w.budget))]   # whole splits
+            idx[b, 0] = _spoil(sel, int(sl[b]), marks)
+        out = torch.empty((w.batch, w.num_q_heads, 512), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+        L.jssa_attend(shape, case.q.to(DEV), case.latent.to(DEV), None, case.block_table.to(DEV),
+                      case.seq_lens.to(DEV), torch.from_numpy(idx).to(DEV), w.sm_scale, out,
+                      L.alloc_workspace(shape), lse)
+        got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+        assert np.isfinite(got).all()
+        for b in range(w.batch):
+            ok = idx[b, 0][(idx[b, 0] >= 0) & (idx[b, 0] < int(sl[b]))]
+            o, lref = omla.attend(q[b], rows[b][ok], w.sm_scale)
+            check_attention(got[b], o)
+            assert np.all(np.abs(glse[b] - lref) <= 1e-3), np.abs(glse[b] - lref).max()
