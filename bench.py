@@ -441,14 +441,17 @@ def _kernel_group(name):
     return None
 
 
-# counters whose instances (one per XCD) are combined with max, as the rocprofv3 derived metrics do; the
-# others are summed over their instances
+# counters with one instance per XCD that the rocprofv3 derived metrics reduce with max (the elapsed cycles
+# of the dispatch); the others are summed over their instances.  rocprofv3's CSV holds one row per (dispatch,
+# counter) with the instances already summed, so such a row is divided by the XCD count (on this GPU the 1 GiB
+# probe's GRBM_GUI_ACTIVE row reads 8 x 2.4 GHz x its traced duration); rows given per instance take the max.
 MAX_OVER_INSTANCES = ("GRBM_GUI_ACTIVE",)
+XCD_NUM = 8
 
 
 def _per_dispatch(d):
     """{kernel group: {counter: mean over the group's dispatches of the counter within a dispatch (summed over
-    its instances, or their max for MAX_OVER_INSTANCES)}}."""
+    its instances, or reduced with max for MAX_OVER_INSTANCES)}}."""
     acc = {}
     for r in _rows(d, "counter_collection.csv"):
         g = _kernel_group(r.get("Kernel_Name", ""))
@@ -456,14 +459,17 @@ def _per_dispatch(d):
             continue
         key = r.get("Dispatch_Id") or r.get("Correlation_Id")
         name, v = r["Counter_Name"], float(r["Counter_Value"])
-        per = acc.setdefault(g, {}).setdefault(name, {})
-        if name in MAX_OVER_INSTANCES:
-            per[key] = max(per.get(key, v), v)
-        else:
-            per[key] = per.get(key, 0.0) + v
+        acc.setdefault(g, {}).setdefault(name, {}).setdefault(key, []).append(v)
     out = {}
     for g, cs in acc.items():
-        out[g] = {c: sum(v.values()) / len(v) for c, v in cs.items()}
+        red = {}
+        for c, per in cs.items():
+            if c in MAX_OVER_INSTANCES:
+                vals = [v[0] / XCD_NUM if len(v) == 1 else max(v) for v in per.values()]
+            else:
+                vals = [sum(v) for v in per.values()]
+            red[c] = sum(vals) / len(vals)
+        out[g] = red
         out[g]["dispatches"] = max(len(v) for v in cs.values())
     return out
 

@@ -61,7 +61,11 @@ def test_counter_summary_derives_request_size_from_probe(tmp_path):
         [1, st, "GRBM_GUI_ACTIVE", 1000.0], [1, st, "GRBM_GUI_ACTIVE", 990.0],   # per-XCD instances: max
         [1, st, "SQ_ACTIVE_INST_VALU", 64000.0],
         [1, st, "SQ_VALU_MFMA_BUSY_CYCLES", 0.0], [1, st, "SQ_LDS_BANK_CONFLICT", 2560.0],
-        [1, st, "SQ_INSTS_LDS", 5.0], [1, st, "SQ_WAVES", 7.0], [1, st, "SQ_BUSY_CU_CYCLES", 1.0]])
+        [1, st, "SQ_INSTS_LDS", 5.0], [1, st, "SQ_WAVES", 7.0], [1, st, "SQ_BUSY_CU_CYCLES", 1.0],
+        # one summed row per dispatch (rocprofv3's own CSV): the per-XCD cycles are the row / 8
+        [3, neg, "GRBM_GUI_ACTIVE", 8000.0], [3, neg, "SQ_ACTIVE_INST_VALU", 25600.0],
+        [3, neg, "SQ_VALU_MFMA_BUSY_CYCLES", 0.0], [3, neg, "SQ_LDS_BANK_CONFLICT", 0.0],
+        [3, neg, "SQ_INSTS_LDS", 0.0], [3, neg, "SQ_WAVES", 1.0]])
     r = bench.summarize_counters(str(rd), str(wr), str(sq), "llama8b_128k", {"select_stream": 254_080}, "cmd")
     assert r["probe"]["bytes_per_read_request"] == 128.0
     assert r["probe"]["fetch_size_definition_bytes"] == 2 ** 30 // 2
@@ -72,6 +76,8 @@ def test_counter_summary_derives_request_size_from_probe(tmp_path):
     assert k["l2_hit_rate"] == 0.3 and k["dispatches"] == 2
     assert k["valu_busy_pct"] == 25.0 and k["mfma_busy_pct"] == 0.0 and k["lds_bank_conflict_pct"] == 1.0
     assert k["traffic_over_algorithmic"] == round((k["read_bytes"] + k["write_bytes"]) / 254_080, 4)
+    n = r["kernels"][bench.PROBE_KERNEL]
+    assert n["gui_active_cycles"] == 1000 and n["valu_busy_pct"] == 10.0
     json.dumps(r)
     assert "select_stream" in bench.counters_markdown(r)
 
