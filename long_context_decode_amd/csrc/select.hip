@@ -143,8 +143,9 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     // about 32 samples per expected selection (so that ks, the sampled keys
     // above tau, is about 64: the candidate count then varies by about 1/8),
     // at least 1024 (where that floor applies, ks = 2B 1024 / N >= 64), and
-    // no more than 256 KB of scoring cache (one CU reads the whole sample)
-    constexpr int kByteCap = (256 * 1024) / (RP * 16);
+    // no more than 128 KB of scoring cache (one CU reads the whole sample, in
+    // one round of loads up to 128-byte tokens)
+    constexpr int kByteCap = (128 * 1024) / (RP * 16);
     int64_t want = (int64_t)32 * N / a.B;
     if (want > kByteCap) want = kByteCap;
     if (want < 1024) want = 1024;
@@ -257,13 +258,16 @@ __global__ __launch_bounds__(kPrologueThreads) void select_prologue(SelectArgs a
     } else if (o < a.r) {
       const float* m = Mh + (int64_t)o * dm + part * 4;
       const double* qb = qbar + part * 4;
-      for (int k0 = 0; k0 < nf; k0 += 8) {     // 8 loads in flight per batch
-        float4 mv[8];
+      // all 16 loads (d = 512) in flight together, 8 when the sample rows in
+      // flight beside them are BF16 keys of more than 128 bytes
+      constexpr int MB = RP > 8 ? 8 : 16;
+      for (int k0 = 0; k0 < nf; k0 += MB) {
+        float4 mv[MB];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < MB; ++k)
           if (k0 + k < nf) mv[k] = *reinterpret_cast<const float4*>(m + (k0 + k) * 32);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < MB; ++k) {
           if (k0 + k < nf) {
             const double* qq = qb + (k0 + k) * 32;
             v = __builtin_fma((double)mv[k].x, qq[0], v);
