@@ -123,9 +123,10 @@ int32_t make_plan(const jssa_shape* sh, Plan* p) {
   p->dv = p->mla ? kMlaLatent : p->d;
   p->maxN = (int64_t)p->max_pages * p->P;
   // stream chunk: the pages one wavefront scores for one KV head, 64 / P pages
-  // per round and 16 / (16-byte pieces per token) rounds
+  // per round and 16 / (16-byte pieces per token) rounds, in two passes for
+  // tokens of 8 or more pieces
   const int pieces = (p->sfmt == JSSA_KEYS_BF16 ? 2 : 1) * (p->S / 16);
-  p->cp = (64 / p->P) * std::max(1, 16 / pieces);
+  p->cp = (64 / p->P) * std::max(1, 16 / pieces) * (pieces >= 8 ? 2 : 1);
   p->heads_pb = std::min(p->Hkv, kStreamWaves);
   p->chunks_pb = kStreamWaves / p->heads_pb;
   p->max_chunks = (int)cdiv(p->max_pages, p->cp);

@@ -348,7 +348,10 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
   constexpr int RP = TokenPieces<R, BF>::value;
   constexpr int PR = 64 / P;                   // pages of one round: lane = (page of the round, slot)
   constexpr int NR = RP >= 16 ? 1 : 16 / RP;   // rounds (tokens per lane), all loads in flight together
-  constexpr int WP = NR * PR;                  // pages of a wavefront = one chunk
+  // passes of NR rounds per wavefront: two for tokens of 8 or more pieces
+  // (MLA), so that a chunk covers 4 pages and the finish has half the regions
+  constexpr int NP = RP >= 8 ? 2 : 1;
+  constexpr int WP = NP * NR * PR;             // pages of a wavefront = one chunk
   constexpr int RL = WP * P + kRegionPad;      // entries of one (chunk, KV head) region
   __shared__ __align__(16) uint2 stage[kStreamWaves][WP * P];
   const int lane = lane_id();
@@ -401,8 +404,20 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
   uint2* st = stage[threadIdx.x >> 6];
   uint32_t cnt = 0;
 #pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
+    if constexpr (NP > 1) {
+      if (pass > 0) {                          // the next pass's rows (pass 0's were loaded above)
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const int pg = (pass * NR + k) * PR + pr;
+          const int64_t phys = __shfl(phys_l, pg);
+          if (page0 + pg < n_pages) load_token_sf<RP, SF>(a, phys, head, slot, pc[k], sc[k]);
+        }
+      }
+    }
+#pragma unroll
   for (int k = 0; k < NR; ++k) {
-    const int t = (page0 + k * PR + pr) * P + slot;
+    const int t = (page0 + (pass * NR + k) * PR + pr) * P + slot;
     uint32_t key = 0u;
     if (t < N) {
       const float s = score_token<R, BF>(pc[k], qh) * sc[k];
@@ -412,6 +427,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream(SelectArgs a) {
     const uint64_t m = ballot(key >= tau);
     if (m & (1ull << lane)) st[cnt + lanes_below(m)] = make_uint2(key, (uint32_t)t);
     cnt += (uint32_t)__popcll(m);
+  }
   }
   // the staged entries were written by this wavefront's own LDS instructions,
   // which complete in order; wait for them before reading them back
