@@ -22,6 +22,11 @@
  *   - Arguments are validated on the host before anything is launched; on
  *     error nothing is enqueued and a negative jssa_status is returned.
  *     A failed launch returns JSSA_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Alignment: q, k_cache, v_cache, k_new, M, kp, workspace and the
+ *     calibration inputs q_cal, k_cal are 16-byte aligned (the kernels read
+ *     them with 16-byte vector loads); every other device pointer is 4-byte
+ *     aligned.  Allocations from hipMalloc or torch are.  A misaligned
+ *     pointer returns JSSA_ERR_ALIGN before anything is launched.
  *   - Caller obligations that are NOT checked on the device: every
  *     block_table entry used (positions < seq_lens[b]) names a valid page;
  *     seq_lens[b] <= max_pages_per_seq * page_size (larger values are clamped);
@@ -72,7 +77,8 @@ typedef enum {
   JSSA_ERR_SHAPE = -2,        /* inconsistent sizes (e.g. Hq % Hkv != 0, budget <= 0) */
   JSSA_ERR_UNSUPPORTED = -3,  /* valid but not built (e.g. d not in {128, 256}) */
   JSSA_ERR_WORKSPACE = -4,    /* workspace smaller than jssa_workspace_bytes() */
-  JSSA_ERR_HIP = -5           /* a HIP launch or runtime call failed */
+  JSSA_ERR_HIP = -5,          /* a HIP launch or runtime call failed */
+  JSSA_ERR_ALIGN = -6         /* a device pointer is not aligned as the conventions require */
 } jssa_status;
 
 enum { JSSA_KIND_GQA = 0, JSSA_KIND_MLA = 1 };

@@ -18,7 +18,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libjssa.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
 KIND_GQA, KIND_MLA = 0, 1
 SELECT_AUTO, SELECT_EXACT_STREAM, SELECT_SPLIT, SELECT_FUSED = 0, 1, 2, 3
 SCALE_FP32, SCALE_E8M0, SCALE_NONE, KEYS_BF16 = 0, 1, 2, 3

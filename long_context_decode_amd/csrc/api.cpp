@@ -181,11 +181,20 @@ T* at(void* ws, size_t off) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? JSSA_OK : JSSA_ERR_HIP; }
 
+// The alignment conventions of the ABI (a NULL pointer passes): vector-read
+// tensors on 16 bytes, every other device pointer on 4.
+bool al(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+template <typename... T>
+bool al16(const T*... p) { return (al(p, 16) && ...); }
+template <typename... T>
+bool al4(const T*... p) { return (al(p, 4) && ...); }
+
 int32_t do_store(const Plan& p, const uint16_t* k_new, const int32_t* slot, int32_t T, const float* M,
                  uint8_t* kp, void* kp_scale, hipStream_t stream) {
   if (T < 0) return JSSA_ERR_SHAPE;
   if (T == 0) return JSSA_OK;
   if (!k_new || !slot || !M || !kp || (!kp_scale && !scale_free(p.sfmt))) return JSSA_ERR_NULL;
+  if (!al16(k_new, M, kp) || !al4(slot, kp_scale)) return JSSA_ERR_ALIGN;
   StoreArgs a{};
   a.k_new = k_new;
   a.slot = slot;
@@ -209,6 +218,8 @@ int32_t do_select(const Plan& p, int select_mode, int stages, const uint16_t* q,
                   const int32_t* slot_new = nullptr) {
   if (!q || !M || !kp || (!kp_scale && !scale_free(p.sfmt)) || !block_table || !seq_lens || !indices || !ws)
     return JSSA_ERR_NULL;
+  if (!al16(q, M, kp, ws, k_new) || !al4(kp_scale, block_table, seq_lens, indices, scores_out, slot_new))
+    return JSSA_ERR_ALIGN;
   if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
   SelectArgs a{};
   a.q = q;
@@ -308,6 +319,7 @@ int32_t do_attend(const Plan& p, const uint16_t* q, const uint16_t* k_cache, con
                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* indices, int window,
                   float sm_scale, uint16_t* out, float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !out || !ws) return JSSA_ERR_NULL;
+  if (!al16(q, k_cache, v_cache, ws) || !al4(block_table, seq_lens, indices, out, lse_out)) return JSSA_ERR_ALIGN;
   if (ws_bytes < p.total) return JSSA_ERR_WORKSPACE;
   if (window < 0) return JSSA_ERR_SHAPE;
   return run_attend(p, q, k_cache, v_cache, block_table, seq_lens, indices, window, sm_scale, out, lse_out,
@@ -328,6 +340,7 @@ const char* jssa_status_string(int32_t status) {
     case JSSA_ERR_SHAPE: return "inconsistent shape";
     case JSSA_ERR_UNSUPPORTED: return "unsupported configuration";
     case JSSA_ERR_WORKSPACE: return "workspace too small";
+    case JSSA_ERR_ALIGN: return "misaligned device pointer";
     case JSSA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -425,6 +438,7 @@ int32_t jssa_attend_noalloc(const jssa_shape* shape, const uint16_t* q, const ui
   const int32_t st = make_plan(shape, &p);
   if (st != JSSA_OK) return st;
   if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !indices || !out) return JSSA_ERR_NULL;
+  if (!al16(q, k_cache, v_cache) || !al4(block_table, seq_lens, indices, out, lse_out)) return JSSA_ERR_ALIGN;
   // the partials of this call's split plan, laid out from the start of the
   // library's scratch array: o [batch, Hq, splits * parts, dv], then (m, l)
   int splits = 0, len = 0;
@@ -451,6 +465,9 @@ int32_t jssa_decode(const jssa_shape* shape, const uint16_t* q, const uint16_t* 
     return JSSA_ERR_NULL;
   if (!p.mla && !v_cache) return JSSA_ERR_NULL;
   if (k_new && !slot_new) return JSSA_ERR_NULL;
+  if (!al16(q, k_new, M, kp, k_cache, v_cache, workspace) ||
+      !al4(slot_new, kp_scale, block_table, seq_lens, indices, out, lse_out))
+    return JSSA_ERR_ALIGN;
   if (workspace_bytes < p.total) return JSSA_ERR_WORKSPACE;
   int32_t single = 0;
   st = jssa_decode_path(shape, &single);
@@ -512,6 +529,8 @@ int32_t jssa_gather_attend(const jssa_shape* shape, const uint16_t* q, const uin
   if (st != JSSA_OK) return st;
   if (!q || !k_cache || (!v_cache && !p.mla) || !block_table || !seq_lens || !indices || !out || !workspace)
     return JSSA_ERR_NULL;
+  if (!al16(q, k_cache, v_cache, workspace) || !al4(block_table, seq_lens, indices, out, lse_out))
+    return JSSA_ERR_ALIGN;
   if (workspace_bytes < p.total) return JSSA_ERR_WORKSPACE;
   GatherArgs g{};
   g.k_cache = k_cache;
@@ -559,6 +578,7 @@ int32_t jssa_calib_moments(const jssa_shape* shape, const uint16_t* q_cal, const
   if (st != JSSA_OK) return st;
   if (T == 0) return JSSA_OK;
   if (!q_cal || !k_cal || !gq || !gk || !workspace) return JSSA_ERR_NULL;
+  if (!al16(q_cal, k_cal, workspace) || !al4(gq, gk)) return JSSA_ERR_ALIGN;
   if (workspace_bytes < need) return JSSA_ERR_WORKSPACE;
   CalibArgs a{};
   a.q = q_cal;

@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_status_strings():
-    for s in range(-5, 1):
+    for s in range(-6, 1):
         assert L.status_string(s) and L.status_string(s) != "unknown status"
     assert L.status_string(7) == "unknown status"
 
@@ -245,3 +245,52 @@ def test_noalloc_attend_refuses_oversized_and_null_before_any_launch():
     st = lib.jssa_attend_noalloc(ctypes.byref(_shape(budget=0)), fake, fake, fake, fake, fake, fake,
                                  ctypes.c_float(0.1), fake, None, None)
     assert st == -2                                           # JSSA_ERR_SHAPE
+
+
+# (entry point, argument kinds after the shape: "16" / "4" = a device pointer that must be 16- / 4-byte
+# aligned, "i" = an int32 (4), "f" = the softmax scale, "z" = workspace bytes (0), "s" = the stream)
+_ALIGN_CASES = [
+    ("jssa_store", ["16", "4", "i", "16", "16", "4", "s"]),
+    ("jssa_select", ["16", "16", "16", "4", "4", "4", "4", "4", "16", "z", "s"]),
+    ("jssa_attend", ["16", "16", "16", "4", "4", "4", "f", "4", "4", "16", "z", "s"]),
+    ("jssa_attend_noalloc", ["16", "16", "16", "4", "4", "4", "f", "4", "4", "s"]),
+    ("jssa_decode", ["16", "16", "4", "16", "16", "4", "16", "16", "4", "4", "4", "f", "4", "4", "16", "z", "s"]),
+    ("jssa_full_decode", ["16", "16", "16", "4", "4", "i", "f", "4", "4", "16", "z", "s"]),
+    ("jssa_gather_attend", ["16", "16", "16", "4", "4", "4", "f", "4", "4", "16", "z", "s"]),
+    ("jssa_calib_moments", ["16", "16", "i", "4", "4", "16", "z", "s"]),
+]
+
+
+@pytest.mark.parametrize("name,kinds", _ALIGN_CASES, ids=[c[0] for c in _ALIGN_CASES])
+def test_misaligned_device_pointers_are_refused_before_any_launch(name, kinds):
+    """Every device pointer that the kernels read with 16-byte vector loads must be 16-byte aligned, every
+    other one 4-byte aligned; a pointer off by 8 (resp. 2) bytes returns JSSA_ERR_ALIGN, and the same call with
+    every pointer aligned fails only on its zero workspace size.  The fake addresses are never dereferenced:
+    validation ends before anything is launched."""
+    lib = L.raw_library()
+    fn = getattr(lib, name)
+    sh = _shape()
+
+    def args(bad=None):
+        out = []
+        for i, k in enumerate(kinds):
+            if k in ("16", "4"):
+                addr = 1 << 16
+                if i == bad:
+                    addr += 8 if k == "16" else 2
+                out.append(ctypes.c_void_p(addr))
+            elif k == "i":
+                out.append(4)
+            elif k == "f":
+                out.append(ctypes.c_float(0.1))
+            elif k == "z":
+                out.append(0)
+            else:
+                out.append(None)
+        return out
+
+    for i, k in enumerate(kinds):
+        if k in ("16", "4"):
+            assert fn(ctypes.byref(sh), *args(i)) == L.ERR_ALIGN, (name, i)
+    if "z" in kinds:
+        assert fn(ctypes.byref(sh), *args()) == L.ERR_WORKSPACE
