@@ -273,6 +273,27 @@ def time_graph(fn, steps, warmup, n_rep):
     return total, med, p10, p90
 
 
+def time_graph_multi(fn, steps, warmup, n_rep, per_graph=8):
+    """per_graph consecutive steps (rotating the replicas) captured in one HIP graph, as a serving loop
+    captures a whole model step; the graph replayed back to back.  Returns ms per step."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i % n_rep)
+    replays = max(1, steps // per_graph)
+    for _ in range(max(1, warmup // per_graph)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * per_graph)
+
+
 def time_stages(stage_fns, steps, n_rep):
     """Average duration of each stage: `steps` back-to-back launches of that stage alone (rotating the
     replicas) between two HIP events on the current stream, the stream every library call launches on.
@@ -768,6 +789,9 @@ def main():
         graph = {"ms_per_step": round(g_ms, 5), "block_median_ms": round(g_med, 5), "p10_ms": round(g_p10, 5),
                  "p90_ms": round(g_p90, 5), "steps_per_s": round(1e3 / g_ms, 2)}
         print(f"[bench] graph {g_ms:.4f} ms/step", file=sys.stderr, flush=True)
+        gm_ms = time_graph_multi(step, args.steps, args.warmup, n_rep)
+        graph["eight_steps_per_graph_ms_per_step"] = round(gm_ms, 5)
+        print(f"[bench] graph of 8 steps {gm_ms:.4f} ms/step", file=sys.stderr, flush=True)
     ms_full, _, _, _, _ = time_steps(full, max(10, args.steps // 10), max(2, args.warmup // 4), n_rep)
     print(f"[bench] full-KV {ms_full:.4f} ms/step", file=sys.stderr, flush=True)
     paths = None
