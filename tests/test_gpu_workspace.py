@@ -1,12 +1,13 @@
-"""GPU: no result depends on what the caller's workspace held before a call.
+"""GPU: no result depends on what the caller's workspace held before a call, nor on other calls.
 
 The workspace that jssa_workspace_bytes sizes is caller memory with no initialisation requirement
 (include/jssa.h, conventions), so every call must write whatever it later reads back: candidate
 regions and their counts, the projected query and threshold, split-K partials, staged rows.  Each
 path below runs twice on the same inputs, once on a workspace of 0xFF bytes (NaN floats, all-ones
 words, -1 ints) and once on zeros, and everything it writes (indices, bf16 output, lse, the scoring
-cache it stores into) must be bit-identical.  Parity with the oracle is checked elsewhere; this file
-checks independence from the workspace's prior contents.
+cache it stores into) must be bit-identical.  Two decode steps overlapping on two streams must also
+write what serial calls write.  Parity with the oracle is checked elsewhere; this file checks
+independence from the workspace's prior contents and from concurrent calls.
 """
 import numpy as np
 import pytest
@@ -122,3 +123,45 @@ def test_mla_paths_do_not_read_stale_workspace(name):
 
     for run in (decode, dense):
         _same(run)
+
+
+def test_concurrent_calls_on_two_streams_match_serial_calls():
+    """The library keeps no state between calls (include/jssa.h, conventions), so two decode steps
+    on two streams, each with its own workspace, outputs and scoring cache, overlapping on the GPU,
+    write exactly what the same calls write one after the other.  Both streams keep the default
+    priority."""
+    w, case, m32, rows_k, rows_v, stored = _gqa("mid_sampled")
+    lay = case.layers[0]
+    q, kc, vc = lay.q.to(DEV), lay.k_cache.to(DEV), lay.v_cache.to(DEV)
+    bt, sl = case.block_table.to(DEV), case.seq_lens.to(DEV)
+    btn, sln = case.block_table.numpy(), case.seq_lens.numpy()
+    new_slot = torch.from_numpy(np.array([btn[b, (sln[b] - 1) // w.page_size] * w.page_size
+                                          + (sln[b] - 1) % w.page_size for b in range(w.batch)], np.int32)).to(DEV)
+    k_new = torch.from_numpy(np.stack([rows_k[b][-1] for b in range(w.batch)]).view(np.int16)).view(
+        torch.bfloat16).to(DEV)
+
+    def prepare():
+        shape, kp, ks, M = _upload(w, case, m32, stored)
+        idx = torch.empty((w.batch, w.num_kv_heads, w.budget), dtype=torch.int32, device=DEV)
+        out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+        return dict(shape=shape, kp=kp, ks=ks, M=M, idx=idx, out=out, ws=_ws(shape, 0xFF))
+
+    def step(r, reps=4):
+        for _ in range(reps):          # repeated steps: the same token stored again, the same result
+            L.jssa_decode(r["shape"], q, k_new, new_slot, r["M"], r["kp"], r["ks"], kc, vc, bt, sl, r["idx"],
+                          w.sm_scale, r["out"], r["ws"])
+
+    serial = prepare()
+    step(serial)
+    torch.cuda.synchronize()
+    a, b = prepare(), prepare()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        step(a)
+    with torch.cuda.stream(s2):
+        step(b)
+    torch.cuda.synchronize()
+    for r in (a, b):
+        for key in ("idx", "out", "kp", "ks"):
+            assert torch.equal(r[key].contiguous().view(torch.uint8), serial[key].contiguous().view(torch.uint8)), key
